@@ -1,0 +1,261 @@
+// C ABI of the FlashHead library: host-side validation and dispatch to the kernel
+// launchers.  The declarations, argument meanings and error behaviour are in
+// include/flashhead.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/flashhead.h"
+#include "fh_device.h"
+#include "fh_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fh_status fail(fh_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fh_status hip_fail(hipError_t e, const char* what) {
+  return fail(FH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxC = 32768;
+constexpr int64_t kMaxB = 65535;
+constexpr int64_t kMaxTile = 256;
+
+int fmt_of(int32_t dt) { return dt == FH_F32 ? fh::RF_F32 : dt == FH_BF16 ? fh::RF_BF16 : fh::RF_INT4; }
+
+// Checks shared by every entry point that takes a desc.
+fh_status check_desc(const fh_desc* d, bool need_tiles) {
+  if (!d) return fail(FH_ERR_ARG, "desc is NULL");
+  if (d->reserved != 0) return fail(FH_ERR_ARG, "desc.reserved must be 0");
+  if (d->B < 1 || d->d < 1 || d->V < 1 || d->c < 1)
+    return fail(FH_ERR_SHAPE, "B, d, V and c must be >= 1 (B=%lld d=%lld V=%lld c=%lld)",
+                (long long)d->B, (long long)d->d, (long long)d->V, (long long)d->c);
+  if (d->B > kMaxB) return fail(FH_ERR_UNSUPPORTED, "B=%lld exceeds %lld", (long long)d->B, (long long)kMaxB);
+  if (d->V >= (int64_t(1) << 31)) return fail(FH_ERR_UNSUPPORTED, "V must be < 2^31");
+  if (d->V % d->c != 0)
+    return fail(FH_ERR_SHAPE, "c=%lld does not divide V=%lld (clusters must have equal size)",
+                (long long)d->c, (long long)d->V);
+  if (d->h_dtype != FH_F32 && d->h_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "h_dtype must be F32 or BF16");
+  if (d->c_dtype != FH_F32 && d->c_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "c_dtype must be F32 or BF16");
+  if (d->e_dtype != FH_F32 && d->e_dtype != FH_BF16 && d->e_dtype != FH_INT4_G128)
+    return fail(FH_ERR_DTYPE, "e_dtype must be F32, BF16 or INT4_G128");
+  if (d->d % 8 != 0) return fail(FH_ERR_SHAPE, "d=%lld must be a multiple of 8", (long long)d->d);
+  const int64_t b = d->V / d->c;
+  if (need_tiles) {
+    if (b > kMaxTile) return fail(FH_ERR_UNSUPPORTED, "cluster size b=%lld exceeds %lld", (long long)b, (long long)kMaxTile);
+    if (d->c > kMaxC) return fail(FH_ERR_UNSUPPORTED, "c=%lld exceeds %lld", (long long)d->c, (long long)kMaxC);
+  }
+  if (d->e_dtype == FH_INT4_G128 && d->d % 128 != 0)
+    return fail(FH_ERR_SHAPE, "int4 token embeddings need d %% 128 == 0 (d=%lld)", (long long)d->d);
+  auto fits = [&](int32_t dt) {
+    const int f = fmt_of(dt);
+    return fh::chunk_slots(f, (int)d->d) <= fh::max_chunk_slots(f);
+  };
+  if (d->d > 16384 || !fits(d->c_dtype) || !fits(d->e_dtype))
+    return fail(FH_ERR_UNSUPPORTED, "d=%lld too large for these dtypes (bf16 <= 4096, f32 <= 2048, int4 <= 8192)",
+                (long long)d->d);
+  return FH_OK;
+}
+
+fh_status check_sampling(int32_t mode, float tau) {
+  if (mode != FH_GREEDY && mode != FH_SAMPLE) return fail(FH_ERR_ARG, "mode must be FH_GREEDY or FH_SAMPLE");
+  if (mode == FH_SAMPLE && !(tau > 0.f && std::isfinite(tau)))
+    return fail(FH_ERR_ARG, "temperature must be finite and > 0 when sampling (got %g)", (double)tau);
+  return FH_OK;
+}
+
+fh_status check_p(const fh_desc* d, int64_t p) {
+  if (p < 1 || p > d->c) return fail(FH_ERR_ARG, "p=%lld must satisfy 1 <= p <= c=%lld", (long long)p, (long long)d->c);
+  return FH_OK;
+}
+
+fh_status check_ws(const fh_desc* d, int64_t p, void* ws, size_t ws_bytes, fh::Workspace* out) {
+  const fh::Workspace need = fh::carve_workspace(nullptr, (int)d->B, (int)d->c, (int)p);
+  if (!ws) return fail(FH_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < need.bytes)
+    return fail(FH_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, need.bytes);
+  *out = fh::carve_workspace(ws, (int)d->B, (int)d->c, (int)p);
+  return FH_OK;
+}
+
+fh::HeadShape shape_of(const fh_desc* d) {
+  fh::HeadShape s;
+  s.B = (int)d->B;
+  s.d = (int)d->d;
+  s.c = (int)d->c;
+  s.b = (int)(d->V / d->c);
+  s.h_bf16 = d->h_dtype == FH_BF16;
+  s.c_fmt = fmt_of(d->c_dtype);
+  s.e_fmt = fmt_of(d->e_dtype);
+  return s;
+}
+
+fh::Sampling sampling_of(int32_t mode, float tau, uint64_t seed, uint64_t step) {
+  return fh::Sampling{mode == FH_SAMPLE ? 1 : 0, tau, seed, step};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* flashhead_version(void) { return "flashhead 0.1.0 gfx950"; }
+
+const char* flashhead_last_error(void) { return g_last_error.c_str(); }
+
+fh_status flashhead_workspace_bytes(const fh_desc* desc, int64_t p, size_t* bytes) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if (!bytes) return fail(FH_ERR_ARG, "bytes is NULL");
+  *bytes = fh::carve_workspace(nullptr, (int)desc->B, (int)desc->c, (int)p).bytes;
+  return FH_OK;
+}
+
+fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E, const int32_t* cluster_tokens,
+                         void* E_tiles, void* E_scales, void* stream) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (src_dtype != FH_F32 && src_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "src_dtype must be F32 or BF16");
+  if (!E || !cluster_tokens || !E_tiles) return fail(FH_ERR_ARG, "E, cluster_tokens and E_tiles must be non-NULL");
+  const bool int4 = desc->e_dtype == FH_INT4_G128;
+  if (int4 && !E_scales) return fail(FH_ERR_ARG, "E_scales must be non-NULL for INT4_G128");
+  if (!int4 && E_scales) return fail(FH_ERR_ARG, "E_scales must be NULL unless e_dtype is INT4_G128");
+  hipStream_t s = (hipStream_t)stream;
+  const int V = (int)desc->V;
+  uint32_t* scratch = nullptr;   // counts[V], bad
+  hipError_t e = hipMalloc(&scratch, (size_t)(V + 1) * sizeof(uint32_t));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  e = hipMemsetAsync(scratch, 0, (size_t)(V + 1) * sizeof(uint32_t), s);
+  if (e == hipSuccess)
+    e = fh::launch_pack(V, (int)desc->d, (int)desc->c, (int)(desc->V / desc->c), src_dtype == FH_BF16,
+                        fmt_of(desc->e_dtype), E, cluster_tokens, E_tiles, (uint16_t*)E_scales, scratch,
+                        scratch + V, s);
+  uint32_t bad = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, scratch + V, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipError_t e2 = hipFree(scratch);
+  if (e != hipSuccess) return hip_fail(e, "flashhead_pack");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+  if (bad) return fail(FH_ERR_ARG, "cluster_tokens is not a permutation of [0, V)");
+  return FH_OK;
+}
+
+fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const void* centroids, int32_t mode,
+                                    float temperature, uint64_t seed, uint64_t step, void* workspace,
+                                    size_t workspace_bytes, float* keys_out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if (!h || !centroids) return fail(FH_ERR_ARG, "h and centroids must be non-NULL");
+  fh::Workspace ws;
+  if ((st = check_ws(desc, 1, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  hipError_t e = fh::launch_scores(shape_of(desc), h, centroids, sampling_of(mode, temperature, seed, step), ws,
+                                   keys_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
+  return FH_OK;
+}
+
+fh_status flashhead_select_probes(const fh_desc* desc, int64_t p, void* workspace, size_t workspace_bytes,
+                                  int32_t* probe_ids_out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  fh::Workspace ws;
+  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  hipError_t e = fh::launch_select(shape_of(desc), (int)p, ws, probe_ids_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "probe selection launch");
+  return FH_OK;
+}
+
+static fh_status check_tiles_args(const fh_desc* desc, const void* h, const int32_t* c2t, const void* tiles,
+                                  const void* scales, const fh_outputs* out) {
+  if (!h || !c2t || !tiles) return fail(FH_ERR_ARG, "h, cluster_tokens and E_tiles must be non-NULL");
+  const bool int4 = desc->e_dtype == FH_INT4_G128;
+  if (int4 && !scales) return fail(FH_ERR_ARG, "E_scales must be non-NULL for INT4_G128");
+  if (!out || !out->token) return fail(FH_ERR_ARG, "out and out->token must be non-NULL");
+  return FH_OK;
+}
+
+fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h, const int32_t* cluster_tokens,
+                                 const void* E_tiles, const void* E_scales, int32_t mode, float temperature,
+                                 uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                                 const fh_outputs* out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if ((st = check_tiles_args(desc, h, cluster_tokens, E_tiles, E_scales, out)) != FH_OK) return st;
+  fh::Workspace ws;
+  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  hipError_t e = fh::launch_tiles(shape_of(desc), (int)p, h, cluster_tokens, E_tiles, (const uint16_t*)E_scales,
+                                  sampling_of(mode, temperature, seed, step), ws, out->probe_logits,
+                                  out->probe_tokens, out->token, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "probe logits launch");
+  return FH_OK;
+}
+
+fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
+                            const void* E_tiles, const void* E_scales, int64_t p, int32_t mode, float temperature,
+                            uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                            const fh_outputs* out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if (!centroids) return fail(FH_ERR_ARG, "centroids must be non-NULL");
+  if ((st = check_tiles_args(desc, h, cluster_tokens, E_tiles, E_scales, out)) != FH_OK) return st;
+  fh::Workspace ws;
+  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  const fh::HeadShape s = shape_of(desc);
+  const fh::Sampling smp = sampling_of(mode, temperature, seed, step);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
+  if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
+  e = fh::launch_select(s, (int)p, ws, out->probe_ids, hs);
+  if (e != hipSuccess) return hip_fail(e, "probe selection launch");
+  e = fh::launch_tiles(s, (int)p, h, cluster_tokens, E_tiles, (const uint16_t*)E_scales, smp, ws, out->probe_logits,
+                       out->probe_tokens, out->token, hs);
+  if (e != hipSuccess) return hip_fail(e, "probe logits launch");
+  return FH_OK;
+}
+
+fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (!bytes) return fail(FH_ERR_ARG, "bytes is NULL");
+  *bytes = fh::dense_workspace_bytes((int)desc->B);
+  return FH_OK;
+}
+
+fh_status flashhead_dense_forward(const fh_desc* desc, const void* h, const void* E, int32_t mode, float temperature,
+                                  uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                                  int32_t* token, float* logits, void* stream) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (desc->e_dtype == FH_INT4_G128) return fail(FH_ERR_DTYPE, "the dense head takes F32 or BF16 E");
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if (!h || !E || !token) return fail(FH_ERR_ARG, "h, E and token must be non-NULL");
+  if (!workspace) return fail(FH_ERR_WORKSPACE, "workspace is NULL");
+  const size_t need = fh::dense_workspace_bytes((int)desc->B);
+  if (workspace_bytes < need)
+    return fail(FH_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes, need);
+  hipError_t e = fh::launch_dense(shape_of(desc), (int)desc->V, h, E, sampling_of(mode, temperature, seed, step),
+                                  (uint64_t*)workspace, token, logits, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dense head launch");
+  return FH_OK;
+}
+
+}  // extern "C"

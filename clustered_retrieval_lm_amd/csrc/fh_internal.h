@@ -1,0 +1,57 @@
+// Internal interface between the C-ABI layer (fh_api.hip) and the kernel launchers
+// (fh_kernels.hip).  Launchers enqueue work on a stream and return the launch status;
+// every shape and pointer has been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fh {
+
+struct HeadShape {
+  int B, d, c, b;     // rows of h, hidden size, clusters, tokens per cluster
+  int h_bf16;         // h storage: 1 = bf16, 0 = f32
+  int c_fmt;          // RowFmt of the centroids
+  int e_fmt;          // RowFmt of the tiles / dense E
+};
+
+struct Sampling {
+  int sample;         // 0 greedy, 1 sampling
+  float tau;
+  uint64_t seed, step;
+};
+
+// Workspace carve-up (all offsets 256-byte aligned): keys, masks, best, probes; the
+// regions stage 1 writes come first so their offsets do not depend on p.
+struct Workspace {
+  float* keys;        // [B][c] stage-1 keys
+  int32_t* probes;    // [B][p] kept clusters, ascending
+  uint64_t* best;     // [B] packed (key, ~token) maxima
+  uint64_t* mask;     // [c][W] rows that kept cluster k (B > 1 only), W = ceil(B / 64)
+  int W;
+  size_t bytes;
+};
+
+Workspace carve_workspace(void* base, int B, int c, int p);
+size_t dense_workspace_bytes(int B);
+
+// Largest chunk-slot count per lane a row format supports (16-byte chunks, 64 lanes).
+int max_chunk_slots(int fmt);
+int chunk_slots(int fmt, int d);
+
+hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const Sampling& smp,
+                         const Workspace& ws, float* keys_out, hipStream_t st);
+hipError_t launch_select(const HeadShape& s, int p, const Workspace& ws, int32_t* probe_out,
+                         hipStream_t st);
+hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t* c2t,
+                        const void* tiles, const uint16_t* scales, const Sampling& smp,
+                        const Workspace& ws, float* logits_out, int32_t* tokens_out,
+                        int32_t* token, hipStream_t st);
+hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E, const Sampling& smp,
+                        uint64_t* best, int32_t* token, float* logits, hipStream_t st);
+hipError_t launch_pack(int V, int d, int c, int b, int src_bf16, int dst_fmt, const void* E,
+                       const int32_t* c2t, void* tiles, uint16_t* scales, uint32_t* counts,
+                       uint32_t* bad, hipStream_t st);
+
+}  // namespace fh

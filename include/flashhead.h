@@ -1,0 +1,205 @@
+/*
+ * flashhead.h -- C ABI of the FlashHead output head for AMD Instinct MI355X (gfx950).
+ *
+ * FlashHead ("FlashHead: Efficient Drop-In Replacement for the Classification Head in
+ * Language Model Inference", Section 3) replaces the dense LM head z = E h (E: [V][d])
+ * by retrieval over balanced vocabulary clusters:
+ *   1. offline, the V token embeddings are split into c clusters of exactly b = V / c
+ *      tokens by balanced spherical k-means (Section 3.1); C[c][d] holds the centroids
+ *      and C2T[c][b] the token ids of each cluster;
+ *   2. online, the centroid logits C h are computed, p clusters are kept -- the top p
+ *      (greedy) or p drawn without replacement from softmax(C h / tau) (sampling) -- the
+ *      tokens of those clusters are gathered, their logits computed, and the argmax or a
+ *      sample from their softmax is returned (Section 3.2).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked "device" are device memory of the current HIP device; "host"
+ *     pointers are host memory.  The caller owns every buffer; the library never keeps a
+ *     pointer after a call returns and never allocates on the forward path.
+ *   - Arrays are dense and row-major with the shapes given; element types follow the
+ *     fh_dtype fields of fh_desc.  bf16 values are passed as their 16-bit patterns.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     asynchronous: results are valid once the stream has been synchronised.  Calls that
+ *     share a workspace must be ordered on one stream.
+ *   - All argument and shape checks run on the host before anything is enqueued.  A check
+ *     that fails returns its status, enqueues nothing and sets the message returned by
+ *     flashhead_last_error() (thread-local).  A HIP launch error returns FH_ERR_HIP.
+ *   - Device data are not validated on the forward path: ids in C2T must form a
+ *     permutation of [0, V) (flashhead_pack checks this), and NaN inputs give an
+ *     unspecified (but in-bounds) result.
+ *   - Ties: a larger key wins; equal keys go to the smaller cluster id (probe selection)
+ *     or to the smaller vocabulary id (token choice), so p = c reproduces the dense head.
+ *
+ * Random numbers (sampling mode).  Philox4x32-10 (Salmon et al., SC'11) with
+ *   key = (seed mod 2^32, seed >> 32), counter = (n >> 2, row, step mod 2^32,
+ *   ((step >> 32) << 2) | stream), word n & 3, u = (2 (word >> 9) + 1) 2^-24,
+ *   Gumbel noise G = -ln(-ln u).
+ * Stream 0 draws the cluster keys (n = cluster id), stream 1 the token keys (n =
+ * vocabulary id); row is the row of h within the call.
+ */
+#ifndef FLASHHEAD_H_
+#define FLASHHEAD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLASHHEAD_ABI_VERSION 1
+
+typedef enum fh_status {
+    FH_OK = 0,
+    FH_ERR_ARG = 1,          /* null pointer, bad enum value, p out of range, tau <= 0 */
+    FH_ERR_SHAPE = 2,        /* V not a multiple of c, d not a multiple of 8 (128 for int4) */
+    FH_ERR_DTYPE = 3,        /* dtype combination not accepted by this entry point */
+    FH_ERR_UNSUPPORTED = 4,  /* shape beyond this build's limits (see flashhead_forward) */
+    FH_ERR_WORKSPACE = 5,    /* workspace missing or smaller than the *_workspace_bytes size */
+    FH_ERR_HIP = 6           /* a HIP runtime call failed; the message names it */
+} fh_status;
+
+typedef enum fh_dtype {
+    FH_F32 = 0,              /* IEEE float32 */
+    FH_BF16 = 1,             /* bfloat16 bit patterns (uint16) */
+    FH_INT4_G128 = 2         /* token embeddings only: int4 with a bf16 scale per 128 elements */
+} fh_dtype;
+
+typedef enum fh_mode {
+    FH_GREEDY = 0,           /* top-p clusters by centroid logit, then argmax of the gathered logits */
+    FH_SAMPLE = 1            /* Gumbel-top-p clusters, then a Gumbel-max token sample, both at tau */
+} fh_mode;
+
+/* Shapes and element types of one head. */
+typedef struct fh_desc {
+    int64_t B;               /* rows of h per call, >= 1 */
+    int64_t d;               /* hidden size */
+    int64_t V;               /* vocabulary size */
+    int64_t c;               /* clusters; b = V / c tokens per cluster */
+    int32_t h_dtype;         /* FH_F32 | FH_BF16 */
+    int32_t c_dtype;         /* FH_F32 | FH_BF16 (centroids) */
+    int32_t e_dtype;         /* FH_F32 | FH_BF16 | FH_INT4_G128 (token embeddings / tiles) */
+    int32_t reserved;        /* must be 0 */
+} fh_desc;
+
+/* Outputs of a forward call; every pointer is device memory.  Only `token` is required. */
+typedef struct fh_outputs {
+    int32_t* token;          /* [B] chosen vocabulary id per row */
+    int32_t* probe_ids;      /* [B][p] kept clusters, ascending cluster id; may be NULL */
+    float*   probe_logits;   /* [B][p][b] logit of token j of the q-th kept cluster; may be NULL */
+    int32_t* probe_tokens;   /* [B][p][b] vocabulary id of that token (C2T row); may be NULL */
+} fh_outputs;
+
+/* Library version string, e.g. "flashhead 0.1.0 gfx950". */
+const char* flashhead_version(void);
+
+/* Message describing the last non-FH_OK status returned on the calling thread. */
+const char* flashhead_last_error(void);
+
+/*
+ * Workspace size (bytes, device memory) that flashhead_forward and the three stage entry
+ * points need for this desc and p.  Writes it to *bytes (host).  The workspace carries
+ * the centroid keys, probe lists and per-row maxima between the stages of one call; it
+ * needs no initialisation.
+ */
+fh_status flashhead_workspace_bytes(const fh_desc* desc, int64_t p, size_t* bytes);
+
+/*
+ * Offline packing into cluster-major tiles (the paper's dense C2T of Section 3.2,
+ * "Complexity": equal cluster sizes make the tokens of cluster k a fixed-size block).
+ *   E              device, [V][d] token-major embeddings of dtype src_dtype (F32 | BF16)
+ *   cluster_tokens device, int32 [c][b]: C2T, a permutation of [0, V)
+ *   E_tiles        device out: row (k, j) = E[C2T[k][j]] at offset (k b + j) * row size,
+ *                  in desc->e_dtype: F32 / BF16 rows of d values (f32 -> bf16 rounds to
+ *                  nearest even), or INT4_G128 rows of d/2 bytes (element 2i in the low
+ *                  nibble of byte i, two's complement, q = clamp(rne(x / s), -7, 7))
+ *   E_scales       device out, INT4_G128 only: bf16 [c][b][d/128], s = bf16(amax / 7) of each
+ *                  group of 128 elements (s = 0 and q = 0 for an all-zero group); else NULL
+ * The low-bit format is this library's reading of the paper's selective quantization
+ * (Section 3.2, "Quantization note"; Table 5).  Checks that C2T is a permutation:
+ * FH_ERR_ARG if it is not.  This call allocates a small device buffer and synchronises
+ * `stream`.
+ */
+fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E,
+                         const int32_t* cluster_tokens, void* E_tiles, void* E_scales,
+                         void* stream);
+
+/*
+ * Stage 1 (Section 3.2): centroid logits s[r][k] = sum_j h[r][j] C[k][j], fp32 accumulation,
+ * turned into probe keys -- s (greedy) or s / tau + G(U(seed, r, step, 0, k)) (sampling) --
+ * stored in the workspace and, if keys_out (device, float [B][c]) is non-NULL, there too.
+ *   h         device [B][d], desc->h_dtype
+ *   centroids device [c][d], desc->c_dtype
+ */
+fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const void* centroids,
+                                    int32_t mode, float temperature, uint64_t seed, uint64_t step,
+                                    void* workspace, size_t workspace_bytes, float* keys_out,
+                                    void* stream);
+
+/*
+ * Probe selection (Section 3.2): for every row keep the p clusters with the largest stage-1
+ * keys (ties to the smaller cluster id).  With sampling keys this is Gumbel-top-p, i.e. p
+ * clusters drawn without replacement from softmax(s / tau).  Reads the keys the last
+ * flashhead_centroid_scores call left in `workspace`; writes the kept ids, ascending, to
+ * the workspace and, if probe_ids_out (device, int32 [B][p]) is non-NULL, there too.
+ */
+fh_status flashhead_select_probes(const fh_desc* desc, int64_t p, void* workspace,
+                                  size_t workspace_bytes, int32_t* probe_ids_out, void* stream);
+
+/*
+ * Stage 2 (Section 3.2): for every kept cluster k of every row r, the logits
+ * z = E_tiles[k][j] . h[r] (j < b, fp32 accumulation; int4 rows are dequantised to q s)
+ * and the token choice: argmax z (greedy) or argmax z / tau + G(U(seed, r, step, 1, t)),
+ * t = C2T[k][j] (sampling, a Gumbel-max draw from softmax(z / tau) over the gathered
+ * tokens).  Reads the probe lists the last flashhead_select_probes call left in
+ * `workspace`.  Writes out->token and the optional outputs.
+ *   cluster_tokens device int32 [c][b]; E_tiles / E_scales as written by flashhead_pack.
+ */
+fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h,
+                                 const int32_t* cluster_tokens, const void* E_tiles,
+                                 const void* E_scales, int32_t mode, float temperature,
+                                 uint64_t seed, uint64_t step, void* workspace,
+                                 size_t workspace_bytes, const fh_outputs* out, void* stream);
+
+/*
+ * The whole head: stage 1, probe selection and stage 2 as above, enqueued back to back.
+ *   h              device [B][d]
+ *   centroids      device [c][d]
+ *   cluster_tokens device int32 [c][b]
+ *   E_tiles        device, cluster-major tiles (flashhead_pack)
+ *   E_scales       device, INT4_G128 scales, else NULL
+ *   p              1 <= p <= c
+ *   mode           FH_GREEDY | FH_SAMPLE; temperature > 0 (sampling only), applied to both
+ *                  stages; seed / step key the Philox draws
+ *   workspace      device, >= flashhead_workspace_bytes(desc, p)
+ *   out            host struct of device pointers
+ * Limits of this build: d % 8 == 0, d <= 4096 (bf16 rows), <= 2048 (f32 rows), d % 128 == 0
+ * and d <= 8192 (int4 rows); c <= 32768; 1 <= b <= 256; V < 2^31; B <= 65535.
+ */
+fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids,
+                            const int32_t* cluster_tokens, const void* E_tiles,
+                            const void* E_scales, int64_t p, int32_t mode, float temperature,
+                            uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                            const fh_outputs* out, void* stream);
+
+/* Workspace size (bytes) for flashhead_dense_forward. */
+fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes);
+
+/*
+ * The dense head the paper starts from (Section 3): z = E h over all V tokens, then argmax
+ * (greedy) or argmax z / tau + G(U(seed, r, step, 1, t)) (sampling), ties to the smaller id.
+ * The same token keys as flashhead_forward's stage 2, so p = c gives identical tokens.
+ *   E       device [V][d] token-major, desc->e_dtype F32 | BF16
+ *   token   device int32 [B] out
+ *   logits  device float [B][V] out, may be NULL
+ */
+fh_status flashhead_dense_forward(const fh_desc* desc, const void* h, const void* E,
+                                  int32_t mode, float temperature, uint64_t seed, uint64_t step,
+                                  void* workspace, size_t workspace_bytes, int32_t* token,
+                                  float* logits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHHEAD_H_ */
