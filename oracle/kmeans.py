@@ -114,13 +114,24 @@ def objective(En: np.ndarray, a: np.ndarray, c: int) -> float:
     return float(np.sum(1.0 - np.einsum("ij,ij->i", En, Cn[a])))
 
 
-def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str) -> np.ndarray:
-    """Mean of each cluster's raw rows (float64 values), rounded to the stored dtype."""
+def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str, unit: bool = False) -> np.ndarray:
+    """Stored centroids of a clustering, rounded once to out_dtype.
+
+    unit=False: the mean of each cluster's raw rows (float64 values);
+    unit=True:  the normalised sum of the members' normalised rows (Section 3.1's c_k).
+    """
     C2T = np.asarray(C2T, dtype=np.int64)
     c, b = C2T.shape
     cent = np.empty((c, E.shape[1]), dtype=np.float64)
     for lo in range(0, c, _ROW_BLOCK):
-        cent[lo:lo + _ROW_BLOCK] = np.asarray(E[C2T[lo:lo + _ROW_BLOCK]], dtype=np.float64).mean(axis=1)
+        rows = np.asarray(E[C2T[lo:lo + _ROW_BLOCK]], dtype=np.float64)
+        if unit:
+            n = np.linalg.norm(rows, axis=2, keepdims=True)
+            sums = np.where(n > 0, rows / np.where(n > 0, n, 1.0), 0.0).sum(axis=1)
+            sn = np.linalg.norm(sums, axis=1, keepdims=True)
+            cent[lo:lo + _ROW_BLOCK] = np.where(sn > 0, sums / np.where(sn > 0, sn, 1.0), 0.0)
+        else:
+            cent[lo:lo + _ROW_BLOCK] = rows.mean(axis=1)
     return codecs.round_to_bf16(cent) if out_dtype == "bf16" else codecs.round_to_f32(cent)
 
 
