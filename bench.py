@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""FlashHead head throughput on one MI355X.
+
+Workload (default): the Gemma-3-1B head shape of the FlashHead paper's experiments
+(Section 4, Table 4): B = 1, d = 1152, V = 262144 tokens in c = 16384 balanced clusters of 16,
+p = 512 probes, bf16 centroids / tiles / hidden state, greedy decoding.  Inputs are the seeded
+synthetic head of workloads.py with the stored balanced clustering of that head
+(tests/golden/clusters_gemma.npz); centroids and tiles are built on the GPU by the library.
+
+A step is one flashhead_forward call (centroid scores, probe selection, probe logits, token)
+over one hidden state.  Calls are captured in a HIP graph that cycles through R copies of
+(centroids, tiles, h) whose footprint is well above the 256 MB last-level cache, so every call
+reads its bytes from HBM.  Prints one JSON line.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma] [--mode greedy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, B=1):
+    """Bytes a call must read at least: centroids, the kept tiles, their C2T rows, h."""
+    row = {"f32": 4 * wl.d, "bf16": 2 * wl.d, "int4": wl.d // 2 + 2 * (wl.d // 128)}[wl.e_pack]
+    csz = 4 if wl.dtype == "f32" else 2
+    c_bytes = wl.c * wl.d * csz
+    tile_bytes = B * wl.p * wl.b * (row + 4)
+    return c_bytes, tile_bytes, c_bytes + tile_bytes + B * wl.d * csz
+
+
+def time_graph(torch, launch, n_calls, reps, warm_reps=2):
+    """Capture n_calls launches in one graph; return seconds per call over `reps` replays."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n_calls):          # eager warm-up on the capture stream
+            launch(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n_calls):
+            launch(i)
+    for _ in range(warm_reps):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * n_calls), g
+
+
+def cpu_baseline(wl, hd, C2T, budget_s=15.0):
+    """The oracle forward (fp64 NumPy) on the host cores: a bounded sample of calls."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import head as ohead
+    from oracle import kmeans
+    Ev = ohead.decode(hd.E, wl.dtype)
+    C = kmeans.centroids_from_c2t(Ev, C2T, wl.dtype)
+    del Ev
+    tiles = ohead.pack_tiles(hd.E, wl.dtype, C2T, wl.e_pack)
+    ohead.forward(hd.h, wl.dtype, C, wl.dtype, C2T, tiles, wl.p)          # warm-up
+    n, t0 = 0, time.perf_counter()
+    while True:
+        ohead.forward(hd.h, wl.dtype, C, wl.dtype, C2T, tiles, wl.p)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= 200:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n / dt, "unit": "calls/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} greedy oracle.head.forward calls (B=1, full workload shape) in {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2400)
+    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--workload", default="gemma")
+    ap.add_argument("--mode", default="greedy", choices=["greedy", "sample"])
+    ap.add_argument("--rotate", type=int, default=0, help="copies of the head cycled through (0: auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-head comparator")
+    ap.add_argument("--copy-calib", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the FlashHead head is measured on a single MI355X "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from clustered_retrieval_lm_amd import flashhead as fh
+    from clustered_retrieval_lm_amd.head import DeviceHead, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fh.load_library()
+    wl = workloads.WORKLOADS[args.workload]
+    cfile = "int4" if args.workload == "int4_b16" else args.workload
+    C2T = np.load(os.path.join(ROOT, "tests", "golden", f"clusters_{cfile}.npz"))["C2T"]
+    log(f"workload {wl.name}: B={wl.B} d={wl.d} V={wl.V} c={wl.c} p={wl.p} {wl.dtype}/{wl.e_pack}")
+    hd = workloads.make_head(wl)
+    dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.dtype, wl.e_pack, wl.dtype,
+                                   device="cuda", keep_dense=not args.no_dense)
+    h0 = to_device(hd.h, "cuda")
+    c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, wl.B)
+    set_bytes = dev.C.numel() * dev.C.element_size() + dev.tiles.numel() + h0.numel() * 2
+    R = args.rotate or max(2, int(np.ceil(4 * MALL_BYTES / max(alg_bytes, 1))))
+    log(f"rotating {R} copies of (centroids, tiles, h): {R * set_bytes / 2**30:.1f} GiB")
+    Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
+    Ts = [dev.tiles] + [dev.tiles.clone() for _ in range(R - 1)]
+    Ss = [dev.scales] + ([dev.scales.clone() for _ in range(R - 1)] if dev.scales is not None else [None] * (R - 1))
+    Hs = [h0] + [h0.clone() for _ in range(R - 1)]
+    B, p = wl.B, wl.p
+    desc = dev.desc(B)
+    ws = dev.workspace(B, p)
+    out = dev.outputs(B, p, probes=False)
+    fo = fh.make_outputs(out["token"])
+    tau = wl.temperatures[0] if (args.mode == "sample" and wl.temperatures) else 1.0
+    lib = fh.load_library()
+    wsb = ws.numel()
+    import ctypes
+
+    def fwd(i):
+        r = i % R
+        st = lib.flashhead_forward(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(), dev.c2t.data_ptr(),
+                                   Ts[r].data_ptr(), Ss[r].data_ptr() if Ss[r] is not None else None, p,
+                                   fh.MODES[args.mode], tau, wl.sample_seed, i, ws.data_ptr(), wsb,
+                                   ctypes.byref(fo), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+    def scores(i):
+        r = i % R
+        st = lib.flashhead_centroid_scores(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(),
+                                           fh.MODES[args.mode], tau, wl.sample_seed, i, ws.data_ptr(), wsb, None,
+                                           torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+    # ---- whole path: graph of G calls, replayed
+    G = R * max(1, 120 // R)
+    reps = max(1, -(-args.steps // G))
+    warm = max(1, -(-args.warmup // G))
+    steps = reps * G
+    log(f"timing {steps} steps ({reps} replays of a {G}-call graph) after {warm * G} warm-up steps")
+    torch.cuda.synchronize()
+    t_call, g_fwd = time_graph(torch, fwd, G, reps, warm_reps=warm)
+    calls_per_s = 1.0 / t_call
+    log(f"forward: {t_call * 1e6:.2f} us/call, {calls_per_s:.0f} calls/s, "
+        f"{alg_bytes / t_call / 1e9:.0f} GB/s algorithmic")
+    del g_fwd
+
+    # ---- dominant kernel: stage-1 centroid scores, timed alone the same way
+    t_sc, g_sc = time_graph(torch, scores, G, reps, warm_reps=1)
+    sc_bytes = c_bytes + B * wl.d * 2 + B * wl.c * 4
+    log(f"centroid scores: {t_sc * 1e6:.2f} us/launch, {sc_bytes / t_sc / 1e9:.0f} GB/s")
+    del g_sc
+
+    dense = None
+    if not args.no_dense:
+        dws = torch.empty(fh.flashhead_dense_workspace_bytes(dev.desc(B, e_dtype=wl.dtype)), dtype=torch.uint8,
+                          device="cuda")
+        dtok = torch.empty(B, dtype=torch.int32, device="cuda")
+        ddesc = dev.desc(B, e_dtype=wl.dtype)
+        E2 = [dev.E, dev.E.clone()]
+
+        def dense_call(i):
+            st = lib.flashhead_dense_forward(ctypes.byref(ddesc), Hs[i % R].data_ptr(), E2[i % 2].data_ptr(),
+                                             fh.MODES[args.mode], tau, wl.sample_seed, i, dws.data_ptr(),
+                                             dws.numel(), dtok.data_ptr(), None,
+                                             torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        t_d, g_d = time_graph(torch, dense_call, 20, 10, warm_reps=1)
+        dense_bytes = wl.V * wl.d * (2 if wl.dtype == "bf16" else 4)
+        dense = {"calls_per_s": round(1.0 / t_d, 1), "us_per_call": round(t_d * 1e6, 2),
+                 "achieved_GBps": round(dense_bytes / t_d / 1e9, 1), "bytes": dense_bytes,
+                 "speedup": round(t_d / t_call, 2), "byte_ratio": round(dense_bytes / alg_bytes, 2)}
+        log(f"dense head: {t_d * 1e6:.1f} us/call, {dense_bytes / t_d / 1e9:.0f} GB/s; "
+            f"FlashHead speedup {t_d / t_call:.2f}x (byte ratio {dense_bytes / alg_bytes:.2f}x)")
+        del g_d, E2
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b_ = torch.empty_like(a)
+        for _ in range(3):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies")
+
+    cpu = None
+    if not args.no_cpu:
+        log("oracle baseline on the host cores ...")
+        cpu = cpu_baseline(wl, hd, C2T)
+        log(f"oracle: {cpu['value']:.2f} calls/s on {cpu['cores']} threads")
+
+    sc_gbs = sc_bytes / t_sc / 1e9
+    res = {
+        "metric": "head calls/s + achieved HBM GB/s vs dense LM head, B=1 Gemma-3-1B shape",
+        "value": round(calls_per_s, 1),
+        "unit": "calls/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm * G,
+        "ms_per_step": round(t_call * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name} head (B={B}, d={wl.d}, V={wl.V}, c={wl.c}, b={wl.b}, p={p}, "
+                               f"{wl.dtype} C/h, {wl.e_pack} tiles, {args.mode})",
+                   "mode": args.mode, "rotated_copies": R},
+        "achieved_GBps": round(alg_bytes / t_call / 1e9, 1),
+        "algorithmic_bytes": alg_bytes,
+        "roofline": {"bound": "hbm", "kernel": "k_b1_scores (centroid scores)",
+                     "achieved": round(sc_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(sc_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": sc_bytes, "us_per_launch": round(t_sc * 1e6, 3)},
+        "dense": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

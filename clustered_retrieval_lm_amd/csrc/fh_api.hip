@@ -153,6 +153,22 @@ fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E, 
   return FH_OK;
 }
 
+fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void* E, const int32_t* cluster_tokens,
+                              int32_t unit, void* centroids, void* stream) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (src_dtype != FH_F32 && src_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "src_dtype must be F32 or BF16");
+  if (unit != 0 && unit != 1) return fail(FH_ERR_ARG, "unit must be 0 or 1");
+  if (!E || !cluster_tokens || !centroids) return fail(FH_ERR_ARG, "E, cluster_tokens and centroids must be non-NULL");
+  if (desc->V / desc->c > kMaxTile)
+    return fail(FH_ERR_UNSUPPORTED, "cluster size b=%lld exceeds %lld", (long long)(desc->V / desc->c), (long long)kMaxTile);
+  hipError_t e = fh::launch_centroids((int)desc->d, (int)desc->c, (int)(desc->V / desc->c), src_dtype == FH_BF16,
+                                      desc->c_dtype == FH_BF16, unit, E, cluster_tokens, centroids,
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "centroids launch");
+  return FH_OK;
+}
+
 fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const void* centroids, int32_t mode,
                                     float temperature, uint64_t seed, uint64_t step, void* workspace,
                                     size_t workspace_bytes, float* keys_out, void* stream) {
@@ -222,6 +238,12 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
   const fh::HeadShape s = shape_of(desc);
   const fh::Sampling smp = sampling_of(mode, temperature, seed, step);
   hipStream_t hs = (hipStream_t)stream;
+  if (s.B == 1 && s.c_fmt == s.e_fmt) {
+    hipError_t e = fh::launch_forward_b1(s, (int)p, h, centroids, cluster_tokens, E_tiles, (const uint16_t*)E_scales,
+                                         smp, ws, out->probe_ids, out->probe_logits, out->probe_tokens, out->token, hs);
+    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+    return FH_OK;
+  }
   hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
   e = fh::launch_select(s, (int)p, ws, out->probe_ids, hs);

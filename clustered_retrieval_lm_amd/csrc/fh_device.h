@@ -85,10 +85,52 @@ __device__ __forceinline__ float make_key(float z, int sample, float tau, const 
 }
 
 // ---------------------------------------------------------------- wave reductions
+// Sum over the 64 lanes with DPP moves (no LDS traffic): quad swaps, half-row and row
+// mirrors, then row broadcasts 15 and 31 carry the row sums up to lane 63, which is read
+// back as a wave-uniform value.  A fixed 6-level tree: the rounding order never varies.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  v = dpp_add<0xB1, 0xF>(v);    // quad_perm(1,0,3,2)
+  v = dpp_add<0x4E, 0xF>(v);    // quad_perm(2,3,0,1)
+  v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);   // row_mirror
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, BOUND);
+}
+
+// Inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts 15 and 31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i<0x111, 0xF, true>(0, v);   // row_shr:1
+  v += dpp_i<0x112, 0xF, true>(0, v);   // row_shr:2
+  v += dpp_i<0x114, 0xF, true>(0, v);   // row_shr:4
+  v += dpp_i<0x118, 0xF, true>(0, v);   // row_shr:8
+  v += dpp_i<0x142, 0xA, false>(0, v);  // row_bcast:15 into rows 1, 3
+  v += dpp_i<0x143, 0xC, false>(0, v);  // row_bcast:31 into rows 2, 3
   return v;
+}
+
+// Max / min of uint32 over the 64 lanes, returned wave-uniform.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  const int id = MAX ? 0 : -1;
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, (uint32_t)dpp_i<0xB1, 0xF, false>(id, (int)v));
+  v = op(v, (uint32_t)dpp_i<0x4E, 0xF, false>(id, (int)v));
+  v = op(v, (uint32_t)dpp_i<0x141, 0xF, false>(id, (int)v));
+  v = op(v, (uint32_t)dpp_i<0x140, 0xF, false>(id, (int)v));
+  v = op(v, (uint32_t)dpp_i<0x142, 0xA, false>(id, (int)v));
+  v = op(v, (uint32_t)dpp_i<0x143, 0xC, false>(id, (int)v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -116,19 +158,44 @@ struct HRegs {
   float v[CH][Fmt<RF>::EPC];
 };
 
-// Load h (fp32 or bf16 storage, d values) into the chunk layout of row format RF.
+// Load h (fp32 or bf16 storage, d values) into the chunk layout of row format RF with
+// 16-byte loads (d is a multiple of the chunk's value count, so chunks are whole).
 template <int RF, int CH>
 __device__ __forceinline__ void load_h(HRegs<RF, CH>& hr, const void* h, int h_bf16, int d, int lane) {
   constexpr int EPC = Fmt<RF>::EPC;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int e0 = (lane + kWave * i) * EPC;
+    const bool ok = e0 < d;
+    if (h_bf16) {
+      const uint4* src = reinterpret_cast<const uint4*>((const uint16_t*)h + e0);
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      const int idx = e0 + e;
-      float x = 0.f;
-      if (idx < d) x = h_bf16 ? bf16_to_f32(((const uint16_t*)h)[idx]) : ((const float*)h)[idx];
-      hr.v[i][e] = x;
+      for (int v = 0; v < EPC / 8; ++v) {
+        const uint4 w = ok ? src[v] : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hr.v[i][8 * v + 2 * j] = bf16_lo(ws[j]);
+          hr.v[i][8 * v + 2 * j + 1] = bf16_hi(ws[j]);
+        }
+      }
+      if (EPC % 8) {   // f32 rows (4 values) with bf16 h: one 8-byte load
+        const uint2 w = ok ? *reinterpret_cast<const uint2*>((const uint16_t*)h + e0) : make_uint2(0u, 0u);
+        hr.v[i][0] = bf16_lo(w.x);
+        hr.v[i][1] = bf16_hi(w.x);
+        hr.v[i][2] = bf16_lo(w.y);
+        hr.v[i][3] = bf16_hi(w.y);
+      }
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>((const float*)h + e0);
+#pragma unroll
+      for (int v = 0; v < EPC / 4; ++v) {
+        const uint4 w = ok ? src[v] : make_uint4(0u, 0u, 0u, 0u);
+        hr.v[i][4 * v + 0] = __uint_as_float(w.x);
+        hr.v[i][4 * v + 1] = __uint_as_float(w.y);
+        hr.v[i][4 * v + 2] = __uint_as_float(w.z);
+        hr.v[i][4 * v + 3] = __uint_as_float(w.w);
+      }
     }
   }
 }

@@ -19,6 +19,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRPI = 4;          // rows per wave per row-dot step
+constexpr int kB1Threads = 1024; // workgroup size of the B = 1 select + tiles kernel
+constexpr int kB1Workgroups = 256;
 constexpr int kThreads = 256;    // 4 waves
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int d) {
@@ -217,13 +219,12 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
 }
 
 // ------------------------------------------------------------------ probe selection
-// One 1024-thread workgroup per row.  Thread t holds keys [t kpt, (t+1) kpt) as
-// order-preserving uint32.  Four 8-bit radix passes from the top find T, the p-th largest
-// key; then every key > T is kept and, of the keys == T, the ones with the smallest ids.
-// Kept ids are written in ascending order (block scans over the per-thread chunks).
+// k_select: one 1024-thread workgroup per row of keys.  Thread t holds keys
+// [t kpt, (t+1) kpt) as order-preserving uint32; select_boundary finds the p-th largest
+// (ties to the smaller id) and the kept ids are written in ascending order (block scans over
+// the per-thread chunks).
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelMaxPerThread = 32;   // c <= 32768
 
 __device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -252,76 +253,432 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
   return res;
 }
 
+// Selection of the p largest of c keys by one workgroup of NT threads.  Thread t holds, in
+// registers, the keys of ids 4 (t + j NT) + e (j < KV, e < 4) as order-preserving uint32 u
+// (larger key <=> larger u; ties go to the smaller id).  The result is the boundary
+// (Tu, Tid): a key is kept iff u > Tu, or u == Tu and id <= Tid.
+//
+// The candidate interval [ilo, ihi] (in u) starts as all keys.  A pass histograms the
+// candidates into 2048 bins and shrinks the interval to the bin holding the boundary; bins
+// above it hold only larger keys and are kept.  The first two passes use bins linear in the
+// key's float value between the interval's ends (a monotone map that spreads the keys near
+// the boundary, so LDS atomics rarely collide); later passes use power-of-two-wide bins in
+// u, each shrinking the u-span 2048-fold, so a single value is reached within three more
+// passes.  Once at most kCand candidates remain they are ranked exactly by (u desc, id asc);
+// a larger set of equal candidates is ordered by id through the bitmap below.
+//
+// The kept ids are then marked in a bitmap over [0, c); prefix popcounts of its words give
+// the ascending-id rank of every kept cluster.
+constexpr int kSelBins = 2048;
+constexpr int kCand = 256;
+constexpr int kSelKV = 8;                  // uint4 of keys per thread: c <= 32 NT
+constexpr int kMaxWords = 32768 / 32;
+
+struct SelShared {
+  int hist[kSelBins];
+  uint32_t bitmap[kMaxWords];
+  int woff[kMaxWords];
+  uint32_t cu[kCand];
+  int cid[kCand];
+  int wtot[6][16];                         // per-wave partials, one slot per use
+  uint32_t wred[6][16];
+  int ncand;
+  int bdig[3];
+  uint32_t Tu;
+  int Tid;
+};
+
+__device__ __forceinline__ float ord_to_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
+}
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t block_minmax(uint32_t v, uint32_t* wred) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_minmax_u32<MAX>(v);
+  if ((threadIdx.x & 63) == 0) wred[wave] = v;
+  __syncthreads();
+  uint32_t r = wred[0];
+  for (int w = 1; w < nw; ++w) r = MAX ? (wred[w] > r ? wred[w] : r) : (wred[w] < r ? wred[w] : r);
+  return r;
+}
+
+// Exclusive prefix sum over the block (thread order); one barrier.  `wtot` must not be
+// reused before the next barrier.
+__device__ __forceinline__ int block_scan(int v, int* wtot, int& total) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) wtot[wave] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = wtot[w];
+    off += w < wave ? t : 0;
+    tot += t;
+  }
+  total = tot;
+  return off + incl - v;
+}
+
+__device__ __forceinline__ int sel_bin(uint32_t u, bool flin, float lo_f, float inv, uint32_t ilo, int ushift) {
+  if (flin) {
+    const float t = (ord_to_float(u) - lo_f) * inv;
+    return t >= 0.f ? (t < (float)(kSelBins - 1) ? (int)t : kSelBins - 1) : 0;
+  }
+  return (int)((u - ilo) >> ushift);
+}
+
+__device__ __forceinline__ int span_shift(uint32_t ilo, uint32_t ihi) {
+  const uint32_t span = ihi - ilo;                 // bins needed: (span >> s) < kSelBins
+  const int bits = span ? 32 - __clz(span) : 0;
+  return bits > 11 ? bits - 11 : 0;
+}
+
+// Load the c keys (floats, global) into registers as ord keys; clears hist and bitmap.
+template <int KV>
+__device__ __forceinline__ void load_keys(const float* keys, int c, uint32_t (&u)[KV][4], SelShared& S) {
+  const int NT = blockDim.x, tid = threadIdx.x;
+  const bool al = (reinterpret_cast<uintptr_t>(keys) & 15) == 0;
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int id0 = 4 * (tid + j * NT);
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (al && id0 + 4 <= c) {
+      w = *reinterpret_cast<const uint4*>(keys + id0);
+    } else if (id0 < c) {
+      w.x = __float_as_uint(keys[id0]);
+      if (id0 + 1 < c) w.y = __float_as_uint(keys[id0 + 1]);
+      if (id0 + 2 < c) w.z = __float_as_uint(keys[id0 + 2]);
+      if (id0 + 3 < c) w.w = __float_as_uint(keys[id0 + 3]);
+    }
+    u[j][0] = ord_key(__uint_as_float(w.x));
+    u[j][1] = ord_key(__uint_as_float(w.y));
+    u[j][2] = ord_key(__uint_as_float(w.z));
+    u[j][3] = ord_key(__uint_as_float(w.w));
+  }
+  for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
+  for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
+}
+
+template <int KV>
+__device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, int p, SelShared& S,
+                                            uint32_t& Tu, int& Tid) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
+  uint32_t vmax = 0u, vmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (idof(j, e) < c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
+  uint32_t ihi = block_minmax<true>(vmax, S.wred[0]);
+  uint32_t ilo = block_minmax<false>(vmin, S.wred[1]);
+  int need = p, n_in = c;
+  for (int level = 0; level < 8 && n_in > kCand && n_in > need && ilo != ihi; ++level) {
+    const float lo_f = ord_to_float(ilo), hi_f = ord_to_float(ihi);
+    const float inv = (float)kSelBins / (hi_f - lo_f);
+    const bool flin = level < 2 && inv > 0.f && inv < 3.0e38f;
+    const int ushift = span_shift(ilo, ihi);
+    if (level > 0) {
+      for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < KV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (idof(j, e) < c && u[j][e] >= ilo && u[j][e] <= ihi)
+          atomicAdd(&S.hist[sel_bin(u[j][e], flin, lo_f, inv, ilo, ushift)], 1);
+    __syncthreads();
+    // suffix counts from the top bin down: thread t owns bins 2047 - t*BPT - i
+    const int bpt = kSelBins / NT;
+    int local = 0;
+    for (int i = 0; i < bpt; ++i) local += S.hist[kSelBins - 1 - tid * bpt - i];
+    int tot;
+    const int before = block_scan(local, S.wtot[level & 1], tot);
+    if (before < need && before + local >= need) {
+      int acc = before;
+      for (int i = 0; i < bpt; ++i) {
+        const int bin = kSelBins - 1 - tid * bpt - i;
+        const int hc = S.hist[bin];
+        if (acc + hc >= need) { S.bdig[0] = bin; S.bdig[1] = acc; S.bdig[2] = hc; break; }
+        acc += hc;
+      }
+    }
+    __syncthreads();
+    const int b = S.bdig[0];
+    need -= S.bdig[1];
+    n_in = S.bdig[2];
+    uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < KV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = u[j][e];
+        if (idof(j, e) < c && x >= ilo && x <= ihi && sel_bin(x, flin, lo_f, inv, ilo, ushift) == b) {
+          bmax = max(bmax, x);
+          bmin = min(bmin, x);
+        }
+      }
+    ihi = block_minmax<true>(bmax, S.wred[2 + 2 * (level & 1)]);
+    ilo = block_minmax<false>(bmin, S.wred[3 + 2 * (level & 1)]);
+  }
+  // every key with u > ihi is kept; `need` more come from the n_in keys in [ilo, ihi]
+  if (n_in == need) {                         // the whole interval is kept
+    Tu = ilo;
+    Tid = 0x7FFFFFFF;
+    return;
+  }
+  if (n_in <= kCand) {                        // rank the candidates exactly
+    if (tid == 0) S.ncand = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (idof(j, e) < c && u[j][e] >= ilo && u[j][e] <= ihi) {
+          const int slot = atomicAdd(&S.ncand, 1);
+          if (slot < kCand) { S.cu[slot] = u[j][e]; S.cid[slot] = idof(j, e); }
+        }
+    __syncthreads();
+    const int n = S.ncand < kCand ? S.ncand : kCand;
+    for (int t = tid; t < n; t += NT) {
+      const uint32_t ut = S.cu[t];
+      const int it = S.cid[t];
+      int rank = 0;
+      for (int q = 0; q < n; ++q) {
+        const uint32_t uq = S.cu[q];
+        rank += (uq > ut) || (uq == ut && S.cid[q] < it);
+      }
+      if (rank == need - 1) { S.Tu = ut; S.Tid = it; }
+    }
+    __syncthreads();
+    Tu = S.Tu;
+    Tid = S.Tid;
+    return;
+  }
+  // many equal candidates (ilo == ihi): the need-th of them in id order, via the bitmap
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m |= (idof(j, e) < c && u[j][e] == ilo) ? (1u << e) : 0u;
+    const int id0 = idof(j, 0);
+    if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
+  }
+  __syncthreads();
+  const int nwords = (c + 31) >> 5;
+  for (int w0 = 0; w0 < nwords; w0 += NT) {
+    const int w = w0 + tid;
+    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
+    int tot;
+    const int before = block_scan(pc, S.wtot[2], tot) ;
+    if (w < nwords && before < need && before + pc >= need) {
+      uint32_t bits = S.bitmap[w];
+      for (int k = before + 1; k < need; ++k) bits &= bits - 1u;
+      S.Tid = (w << 5) + __ffs(bits) - 1;
+    }
+    need -= tot;
+    __syncthreads();
+  }
+  for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
+  __syncthreads();
+  Tu = ilo;
+  Tid = S.Tid;
+}
+
+// Mark the kept keys in the bitmap and turn its word popcounts into prefix offsets (woff).
+template <int KV>
+__device__ __forceinline__ void mark_kept(const uint32_t (&u)[KV][4], int c, uint32_t Tu, int Tid, SelShared& S) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int id0 = 4 * (tid + j * NT);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = id0 + e;
+      m |= (id < c && (u[j][e] > Tu || (u[j][e] == Tu && id <= Tid))) ? (1u << e) : 0u;
+    }
+    if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
+  }
+  __syncthreads();
+  const int nwords = (c + 31) >> 5;
+  int carry = 0;
+  for (int w0 = 0; w0 < nwords; w0 += NT) {
+    const int w = w0 + tid;
+    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
+    int tot;
+    const int before = block_scan(pc, S.wtot[4 + ((w0 / NT) & 1)], tot);
+    if (w < nwords) S.woff[w] = carry + before;
+    carry += tot;
+  }
+  __syncthreads();
+}
+
+// Cluster id of ascending rank q among the kept ones (binary search over the word offsets).
+__device__ __forceinline__ int kept_at(const SelShared& S, int nwords, int q) {
+  int lo = 0, hi = nwords - 1;
+  while (lo < hi) {                          // last word with woff <= q
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.woff[mid] <= q) lo = mid; else hi = mid - 1;
+  }
+  uint32_t bits = S.bitmap[lo];
+  for (int k = S.woff[lo]; k < q; ++k) bits &= bits - 1u;
+  return (lo << 5) + __ffs(bits) - 1;
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c, int p, int32_t* probes,
                                                         int32_t* probe_out, uint64_t* mask, int W,
                                                         uint64_t* best) {
-  __shared__ int hist[256];
-  __shared__ int scan_sh[17];
-  __shared__ int sh_digit, sh_above;
+  __shared__ SelShared S;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const int kpt = (c + kSelThreads - 1) / kSelThreads;
-  const int lo = tid * kpt;
-  const float* kr = keys + (size_t)r * c;
-  uint32_t u[kSelMaxPerThread];
-#pragma unroll
-  for (int i = 0; i < kSelMaxPerThread; ++i) u[i] = (i < kpt && lo + i < c) ? ord_key(kr[lo + i]) : 0u;
-  uint32_t prefix = 0, pmask = 0;
-  int need = p;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
-    if (tid == 0) { sh_digit = 0; sh_above = 0; }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSelMaxPerThread; ++i) {
-      if (i < kpt && lo + i < c && (u[i] & pmask) == prefix) atomicAdd(&hist[(u[i] >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    const int v = tid < 256 ? hist[255 - tid] : 0;
-    int tot;
-    const int ex = block_excl_scan(v, scan_sh, tot);
-    if (tid < 256 && ex < need && ex + v >= need) {
-      sh_digit = 255 - tid;
-      sh_above = ex;
-    }
-    __syncthreads();
-    prefix |= (uint32_t)sh_digit << shift;
-    pmask |= 0xFFu << shift;
-    need -= sh_above;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  int n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < kSelMaxPerThread; ++i) {
-    if (i < kpt && lo + i < c) {
-      n_gt += u[i] > T;
-      n_eq += u[i] == T;
-    }
-  }
-  int tot;
-  const int eq_before = block_excl_scan(n_eq, scan_sh, tot);
-  const int take_eq = min(max(need - eq_before, 0), n_eq);
-  int pos = block_excl_scan(n_gt + take_eq, scan_sh, tot);
-  int32_t* pr = probes + (size_t)r * p;
-  int eq_seen = 0;
-#pragma unroll
-  for (int i = 0; i < kSelMaxPerThread; ++i) {
-    if (i < kpt && lo + i < c) {
-      bool take = u[i] > T;
-      if (u[i] == T) {
-        take = eq_seen < take_eq;
-        ++eq_seen;
-      }
-      if (take && pos < p) {
-        const int k = lo + i;
-        pr[pos] = k;
-        if (probe_out) probe_out[(size_t)r * p + pos] = k;
-        if (mask) atomicOr((unsigned long long*)&mask[(size_t)k * W + (r >> 6)], 1ull << (r & 63));
-        ++pos;
-      }
-    }
+  uint32_t u[kSelKV][4];
+  uint32_t Tu;
+  int Tid;
+  load_keys<kSelKV>(keys + (size_t)r * c, c, u, S);
+  select_regs<kSelKV>(u, c, p, S, Tu, Tid);
+  mark_kept<kSelKV>(u, c, Tu, Tid, S);
+  const int nwords = (c + 31) >> 5;
+  for (int q = tid; q < p; q += kSelThreads) {
+    const int k = kept_at(S, nwords, q);
+    probes[(size_t)r * p + q] = k;
+    if (probe_out) probe_out[(size_t)r * p + q] = k;
+    if (mask) atomicOr((unsigned long long*)&mask[(size_t)k * W + (r >> 6)], 1ull << (r & 63));
   }
   if (tid == 0) best[r] = 0ull;
+}
+
+// ------------------------------------------------------------------ B = 1 fused path
+// Two kernels per call.  k_b1_scores streams C once (GPW row groups per wave, all loads
+// issued before any arithmetic) and writes the keys; its block 0 also clears the per-call
+// state of the second kernel.  k_b1_select_tiles: every workgroup reads the c keys, runs
+// the same radix select (so no grid-wide synchronisation is needed), keeps the probes
+// whose rank q satisfies q % gridDim.x == blockIdx.x, streams their tiles, and the last
+// workgroup to finish turns the packed maximum into the token.
+
+struct B1Params {
+  const void* h;
+  const char* C;
+  int h_bf16, c, d, b, p;
+  int sample;
+  float tau;
+  Rng rng;
+  float* keys;
+  float* keys_out;      // optional copy of the keys (staged entry point)
+  uint64_t* best;
+  uint32_t* done;
+  const int32_t* c2t;
+  const char* tiles;
+  const uint16_t* scales;
+  int32_t* probe_out;
+  float* logits_out;
+  int32_t* tokens_out;
+  int32_t* token;
+};
+
+template <int RF, int CH, int GPW>
+__global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.best[0] = 0ull;
+    a.done[0] = 0u;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nw = gridDim.x * 4;
+  const int rb = row_bytes_of(RF, a.d);
+  HRegs<RF, CH> hr;
+  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
+  for (int k0 = wg * kRPI * GPW; k0 < a.c; k0 += nw * kRPI * GPW) {
+    RowGroup<RF, CH> g[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) rows_load<RF, CH>(g[gi], a.C, rb, k0 + gi * kRPI, a.c, nullptr, 0, lane);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      float s[kRPI];
+      rows_dot<RF, CH>(g[gi], hr, s);
+#pragma unroll
+      for (int i = 0; i < kRPI; ++i) {
+        const int k = k0 + gi * kRPI + i;
+        if (lane == i && k < a.c) {
+          const float key = make_key(s[i], a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
+          a.keys[k] = key;
+          if (a.keys_out) a.keys_out[k] = key;
+        }
+      }
+    }
+  }
+}
+
+template <int RF, int CH, int NT>
+__global__ __launch_bounds__(NT) void k_b1_select_tiles(B1Params a) {
+  constexpr int NWAVE = NT / 64;
+  constexpr int KV = 32768 / (4 * NT);
+  constexpr int MAXLIST = 256;      // probes per workgroup (p <= MAXLIST * gridDim.x)
+  __shared__ SelShared S;
+  __shared__ int my_list[MAXLIST];
+  __shared__ uint64_t wmax[NWAVE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = gridDim.x, me = blockIdx.x;
+  uint32_t u[KV][4];
+  uint32_t Tu;
+  int Tid;
+  load_keys<KV>(a.keys, a.c, u, S);
+  select_regs<KV>(u, a.c, a.p, S, Tu, Tid);
+  mark_kept<KV>(u, a.c, Tu, Tid, S);
+  const int nwords = (a.c + 31) >> 5;
+  const int n_my = me < a.p ? (a.p - me + G - 1) / G : 0;
+  for (int i = tid; i < n_my; i += NT) my_list[i] = kept_at(S, nwords, me + i * G);
+  if (me == 0 && a.probe_out)
+    for (int q = tid; q < a.p; q += NT) a.probe_out[q] = kept_at(S, nwords, q);
+  __syncthreads();
+  // stage 2 on this workgroup's probes
+  const int ngroups = (a.b + kRPI - 1) / kRPI;
+  const int rb = row_bytes_of(RF, a.d);
+  const int spr = a.d >> 7;
+  HRegs<RF, CH> hr;
+  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
+  uint64_t bc = 0;
+  for (int it = wave; it < n_my * ngroups; it += NWAVE) {
+    const int qi = it / ngroups, j0 = (it % ngroups) * kRPI;
+    const int k = my_list[qi];
+    const int q = qi * G + me;
+    int tj[kRPI];
+#pragma unroll
+    for (int i = 0; i < kRPI; ++i) tj[i] = (j0 + i < a.b) ? a.c2t[(size_t)k * a.b + j0 + i] : 0;
+    RowGroup<RF, CH> g;
+    rows_load<RF, CH>(g, a.tiles + (size_t)k * a.b * rb, rb, j0, a.b,
+                      RF == RF_INT4 ? a.scales + (size_t)k * a.b * spr : nullptr, spr, lane);
+    float z[kRPI];
+    rows_dot<RF, CH>(g, hr, z);
+#pragma unroll
+    for (int i = 0; i < kRPI; ++i) {
+      const int j = j0 + i;
+      if (lane == i && j < a.b) {
+        const int t = tj[i];
+        const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
+        const uint64_t cnd = pack_cand(key, (uint32_t)t);
+        bc = cnd > bc ? cnd : bc;
+        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = z[i];
+        if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
+      }
+    }
+  }
+  bc = wave_max_u64(bc);
+  if (lane == 0) wmax[wave] = bc;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t m = wmax[0];
+    for (int w = 1; w < NWAVE; ++w) m = wmax[w] > m ? wmax[w] : m;
+    if (m) atomicMax((unsigned long long*)a.best, (unsigned long long)m);
+    __threadfence();
+    const uint32_t prev = atomicAdd(a.done, 1u);
+    if (prev == (uint32_t)G - 1) {
+      __threadfence();
+      const uint64_t fin = atomicAdd((unsigned long long*)a.best, 0ull);
+      a.token[0] = (int32_t)cand_id(fin);
+    }
+  }
 }
 
 // ------------------------------------------------------------------ stage 2
@@ -564,6 +921,79 @@ __global__ void k_check_counts(const uint32_t* counts, int V, uint32_t* bad) {
   if (i < V && counts[i] != 1u) atomicOr(bad, 2u);
 }
 
+// ------------------------------------------------------------------ cluster centroids
+// C[k] = mean of the b rows E[C2T[k][j]] (or, for unit centroids, the normalised sum of
+// the normalised rows), accumulated in fp64 and rounded once to the stored dtype.
+
+// Round a double to bf16, nearest even, by rounding at the bf16 quantum of its binade.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  if (!(fabs(x) < 0x1p128)) {            // inf, NaN or beyond the bf16 range
+    if (x != x) return 0x7FC0u;
+    return x > 0 ? 0x7F80u : 0xFF80u;
+  }
+  int e;
+  frexp(x, &e);                           // |x| = m 2^e, 0.5 <= m < 1
+  const int qe = e - 8 > -133 ? e - 8 : -133;
+  const double r = ldexp(rint(ldexp(x, -qe)), qe);   // exact scaling, ties to even
+  if (fabs(r) >= 0x1p128) return x > 0 ? 0x7F80u : 0xFF80u;
+  return (uint16_t)(__float_as_uint((float)r) >> 16);   // r has <= 8 significant bits
+}
+
+struct CentroidParams {
+  const char* E;
+  const int32_t* c2t;
+  void* out;
+  int d, b, src_bf16, dst_bf16, unit;
+};
+
+__global__ __launch_bounds__(kThreads) void k_centroids(CentroidParams a) {
+  __shared__ double inv_norm[256];       // b <= 256
+  __shared__ double red[kThreads / kWave];
+  const int k = blockIdx.x, tid = threadIdx.x;
+  const int esz = a.src_bf16 ? 2 : 4;
+  auto val = [&](int row, int e) -> double {
+    const char* src = a.E + ((size_t)row * a.d + e) * esz;
+    return a.src_bf16 ? (double)bf16_to_f32(*(const uint16_t*)src) : (double)*(const float*)src;
+  };
+  const int32_t* rows = a.c2t + (size_t)k * a.b;
+  if (a.unit) {
+    for (int j = 0; j < a.b; ++j) {
+      double ss = 0.0;
+      for (int e = tid; e < a.d; e += kThreads) { const double v = val(rows[j], e); ss += v * v; }
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
+      if ((tid & 63) == 0) red[tid >> 6] = ss;
+      __syncthreads();
+      if (tid == 0) {
+        const double t = (red[0] + red[1]) + (red[2] + red[3]);
+        inv_norm[j] = t > 0.0 ? 1.0 / sqrt(t) : 0.0;
+      }
+      __syncthreads();
+    }
+  }
+  double nsq = 0.0;
+  for (int pass = 0; pass < (a.unit ? 2 : 1); ++pass) {
+    double scale = 1.0;
+    if (a.unit && pass == 1) {
+      if ((tid & 63) == 0) red[tid >> 6] = nsq;
+      __syncthreads();
+      const double t = (red[0] + red[1]) + (red[2] + red[3]);
+      scale = t > 0.0 ? 1.0 / sqrt(t) : 0.0;
+    }
+    for (int e = tid; e < a.d; e += kThreads) {
+      double sum = 0.0;
+      for (int j = 0; j < a.b; ++j) sum += a.unit ? val(rows[j], e) * inv_norm[j] : val(rows[j], e);
+      if (a.unit && pass == 0) { nsq += sum * sum; continue; }
+      const double m = a.unit ? sum * scale : sum / (double)a.b;
+      const size_t o = (size_t)k * a.d + e;
+      if (a.dst_bf16) ((uint16_t*)a.out)[o] = f64_to_bf16_rne(m);
+      else ((float*)a.out)[o] = (float)m;
+    }
+    if (a.unit && pass == 0) {
+      for (int m = 32; m >= 1; m >>= 1) nsq += __shfl_xor(nsq, m, kWave);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host launchers
 
 Workspace carve_workspace(void* base, int B, int c, int p) {
@@ -582,6 +1012,8 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   }
   w.best = (uint64_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * sizeof(uint64_t));
+  w.done = (uint32_t*)(b ? b + off : nullptr);
+  off = up(off + 4 * sizeof(uint32_t));
   w.probes = (int32_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * p * sizeof(int32_t));
   w.bytes = off;
@@ -619,6 +1051,22 @@ int chunk_slots(int fmt, int d) {
     default: return hipErrorInvalidValue;                         \
   }
 
+template <int RF, int CH>
+static void launch_b1_scores(const B1Params& a, int c, hipStream_t st) {
+  constexpr int GPW = CH <= 4 ? 2 : 1;
+  const int groups = (c + kRPI - 1) / kRPI;
+  const int wgs = (groups + 4 * GPW - 1) / (4 * GPW);
+  hipLaunchKernelGGL((k_b1_scores<RF, CH, GPW>), dim3(wgs), dim3(kThreads), 0, st, a);
+}
+
+template <int RF, int CH>
+static void launch_b1_pair(const B1Params& a, int c, int p, hipStream_t st) {
+  launch_b1_scores<RF, CH>(a, c, st);
+  int G = p < kB1Workgroups ? p : kB1Workgroups;
+  if (G < (p + 255) / 256) G = (p + 255) / 256;
+  hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads>), dim3(G), dim3(kB1Threads), 0, st, a);
+}
+
 static bool use_mfma(const HeadShape& s, int fmt) {
   return s.B > 1 && s.h_bf16 && fmt == RF_BF16 && (s.d % 32) == 0;
 }
@@ -646,6 +1094,19 @@ static hipError_t launch_mfma(const MfmaParams& p, int max_wg, hipStream_t st) {
 hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const Sampling& smp,
                          const Workspace& ws, float* keys_out, hipStream_t st) {
   const Rng rng = make_rng(smp.seed, smp.step);
+  if (s.B == 1) {   // the same kernel the fused B = 1 forward runs
+    B1Params a{};
+    a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
+    a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
+    a.keys = ws.keys; a.keys_out = keys_out; a.best = ws.best; a.done = ws.done;
+    const int ch = chunk_slots(s.c_fmt, s.d);
+    if (s.c_fmt == RF_F32) {
+      FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
+    } else {
+      FH_DISPATCH_CH(ch, (launch_b1_scores<RF_BF16, kCH>(a, s.c, st)));
+    }
+    return hipGetLastError();
+  }
   if (use_mfma(s, s.c_fmt)) {
     MfmaParams p{};
     p.H = (const uint16_t*)h;
@@ -671,7 +1132,8 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
 }
 
 hipError_t launch_select(const HeadShape& s, int p, const Workspace& ws, int32_t* probe_out, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(s.B), dim3(kSelThreads), 0, st, (const float*)ws.keys, s.c, p,
+  hipLaunchKernelGGL(k_select, dim3(s.B), dim3(kSelThreads), 0, st,
+                     (const float*)ws.keys, s.c, p,
                      ws.probes, probe_out, ws.mask, ws.W, ws.best);
   return hipGetLastError();
 }
@@ -700,6 +1162,29 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, (const uint64_t*)ws.best, token, s.B);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_b1(const HeadShape& s, int p, const void* h, const void* C, const int32_t* c2t,
+                             const void* tiles, const uint16_t* scales, const Sampling& smp, const Workspace& ws,
+                             int32_t* probe_out, float* logits_out, int32_t* tokens_out, int32_t* token,
+                             hipStream_t st) {
+  B1Params a{};
+  a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
+  a.sample = smp.sample; a.tau = smp.tau; a.rng = make_rng(smp.seed, smp.step);
+  a.keys = ws.keys; a.best = ws.best; a.done = ws.done;
+  a.c2t = c2t; a.tiles = (const char*)tiles; a.scales = scales;
+  a.probe_out = probe_out; a.logits_out = logits_out; a.tokens_out = tokens_out; a.token = token;
+  // the centroid rows and the tile rows may differ in format: dispatch on the pair
+  const int chc = chunk_slots(s.c_fmt, s.d), che = chunk_slots(s.e_fmt, s.d);
+  if (s.c_fmt != s.e_fmt || chc != che) return hipErrorNotSupported;
+  if (s.e_fmt == RF_F32) {
+    FH_DISPATCH_CH(che, (launch_b1_pair<RF_F32, kCH>(a, s.c, p, st)));
+  } else if (s.e_fmt == RF_BF16) {
+    FH_DISPATCH_CH(che, (launch_b1_pair<RF_BF16, kCH>(a, s.c, p, st)));
+  } else {
+    return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 
@@ -732,6 +1217,13 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, (const uint64_t*)best, token, s.B);
+  return hipGetLastError();
+}
+
+hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int unit, const void* E,
+                            const int32_t* c2t, void* out, hipStream_t st) {
+  CentroidParams a{(const char*)E, c2t, out, d, b, src_bf16, dst_bf16, unit};
+  hipLaunchKernelGGL(k_centroids, dim3(c), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

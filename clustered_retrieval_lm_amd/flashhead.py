@@ -64,6 +64,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_last_error": ([], ctypes.c_char_p),
         "flashhead_workspace_bytes": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_pack": ([D, i32, vp, vp, vp, vp, vp], ctypes.c_int),
+        "flashhead_centroids": ([D, i32, vp, vp, i32, vp, vp], ctypes.c_int),
         "flashhead_centroid_scores": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_select_probes": ([D, i64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_probe_logits": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
@@ -151,6 +152,12 @@ def flashhead_pack(desc: fh_desc, src_dtype, E, cluster_tokens, E_tiles, E_scale
     src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
     _check(load_library().flashhead_pack(ctypes.byref(desc), src, _ptr(E), _ptr(cluster_tokens), _ptr(E_tiles),
                                          _ptr(E_scales), _stream(stream)))
+
+
+def flashhead_centroids(desc: fh_desc, src_dtype, E, cluster_tokens, centroids, unit=False, stream=None) -> None:
+    src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
+    _check(load_library().flashhead_centroids(ctypes.byref(desc), src, _ptr(E), _ptr(cluster_tokens), int(bool(unit)),
+                                              _ptr(centroids), _stream(stream)))
 
 
 def flashhead_centroid_scores(desc: fh_desc, h, centroids, mode, temperature, seed, step, workspace,

@@ -14,8 +14,10 @@ from . import flashhead as fh
 _ELEM = {"f32": 4, "bf16": 2}
 
 
-def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+def to_device(a, device="cuda") -> torch.Tensor:
     """Copy a numpy array to the device bit for bit (bf16 bit patterns stay int16)."""
+    if isinstance(a, torch.Tensor):
+        return a.to(device)
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         a = a.view(np.int16)
@@ -32,7 +34,7 @@ class DeviceHead:
         self.c_dtype, self.e_dtype, self.h_dtype, self.e_src = c_dtype, e_dtype, h_dtype, e_src
         self.device = device
         self.C = to_device(centroids, device)
-        self.c2t = to_device(np.asarray(c2t, dtype=np.int32), device)
+        self.c2t = c2t.to(device) if isinstance(c2t, torch.Tensor) else to_device(np.asarray(c2t, np.int32), device)
         Ed = to_device(E, device)
         rows = c * self.b
         if e_dtype == "int4":
@@ -44,6 +46,17 @@ class DeviceHead:
         fh.flashhead_pack(self.desc(1), e_src, Ed, self.c2t, self.tiles, self.scales, stream=stream)
         self.E = Ed if keep_dense else None
         self._ws = {}
+
+    @classmethod
+    def from_clusters(cls, d: int, V: int, c: int, c2t: np.ndarray, E: np.ndarray, e_src: str, c_dtype: str,
+                      e_dtype: str, h_dtype: str, device="cuda", keep_dense=False, unit=False, stream=None):
+        """Build the head from a clustering alone: centroids computed on the GPU."""
+        Ed = to_device(E, device)
+        c2t_d = to_device(np.asarray(c2t, dtype=np.int32), device)
+        cent = torch.empty(c * d * (2 if c_dtype == "bf16" else 4), dtype=torch.uint8, device=device)
+        desc = fh.make_desc(1, d, V, c, h_dtype, c_dtype, e_dtype)
+        fh.flashhead_centroids(desc, e_src, Ed, c2t_d, cent, unit=unit, stream=stream)
+        return cls(d, V, c, cent, c2t_d, Ed, e_src, c_dtype, e_dtype, h_dtype, device, keep_dense, stream)
 
     def desc(self, B: int, e_dtype=None) -> fh.fh_desc:
         return fh.make_desc(B, self.d, self.V, self.c, self.h_dtype, self.c_dtype, e_dtype or self.e_dtype)

@@ -125,6 +125,21 @@ fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E,
                          void* stream);
 
 /*
+ * Offline centroids of a given clustering (Section 3.1, "Centroid matrix").
+ *   E              device, [V][d] token-major embeddings of dtype src_dtype (F32 | BF16)
+ *   cluster_tokens device, int32 [c][b]: C2T
+ *   unit           0: C[k] = mean of the b rows of cluster k;
+ *                  1: C[k] = normalise(sum of the normalised rows), the unit centroid the
+ *                     paper stores (a zero row or sum contributes / gives 0)
+ *   centroids      device out, [c][d] in desc->c_dtype
+ * Sums run in fp64 and are rounded once to the output dtype (bf16: nearest even).  The
+ * forward pass accepts either form.  Asynchronous on `stream`.
+ */
+fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void* E,
+                              const int32_t* cluster_tokens, int32_t unit, void* centroids,
+                              void* stream);
+
+/*
  * Stage 1 (Section 3.2): centroid logits s[r][k] = sum_j h[r][j] C[k][j], fp32 accumulation,
  * turned into probe keys -- s (greedy) or s / tau + G(U(seed, r, step, 0, k)) (sampling) --
  * stored in the workspace and, if keys_out (device, float [B][c]) is non-NULL, there too.
