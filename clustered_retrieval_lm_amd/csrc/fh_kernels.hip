@@ -29,6 +29,13 @@ __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int d) {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// Streaming 16-byte load (non-temporal: rows of C, tiles and E are read once per call).
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ------------------------------------------------------------------ row dot products
 
 template <int RF, int CH>
@@ -49,7 +56,7 @@ __device__ __forceinline__ void rows_load(RowGroup<RF, CH>& g, const char* base,
     for (int i = 0; i < CH; ++i) {
       const int q = lane + kWave * i;
       const bool ok = j < nrows && q < cpr;
-      g.w[r][i] = ok ? ld16(base + (size_t)j * rb + (size_t)q * 16) : make_uint4(0u, 0u, 0u, 0u);
+      g.w[r][i] = ok ? ld16_stream(base + (size_t)j * rb + (size_t)q * 16) : make_uint4(0u, 0u, 0u, 0u);
       g.sc[r][i] = (RF == RF_INT4 && ok) ? bf16_to_f32(scales[(size_t)j * spr + (q >> 2)]) : 0.f;
     }
   }
@@ -550,12 +557,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
 }
 
 // ------------------------------------------------------------------ B = 1 fused path
-// Two kernels per call.  k_b1_scores streams C once (GPW row groups per wave, all loads
-// issued before any arithmetic) and writes the keys; its block 0 also clears the per-call
-// state of the second kernel.  k_b1_select_tiles: every workgroup reads the c keys, runs
-// the same radix select (so no grid-wide synchronisation is needed), keeps the probes
-// whose rank q satisfies q % gridDim.x == blockIdx.x, streams their tiles, and the last
-// workgroup to finish turns the packed maximum into the token.
+// Two kernels per call.  k_b1_scores streams C (one 4-row group per wave, all row loads
+// issued before any arithmetic) and writes the keys; its block 0 clears the per-call state
+// of the second kernel.  k_b1_select_tiles: every workgroup loads the c keys into registers
+// and runs the same exact top-p selection (select_fast), keeps the probes whose rank q
+// satisfies q % gridDim.x == blockIdx.x, streams their tiles, and the last workgroup to
+// finish writes the token.  No workgroup ever waits for another.
 
 struct B1Params {
   const void* h;
@@ -577,7 +584,7 @@ struct B1Params {
   int32_t* token;
 };
 
-template <int RF, int CH, int GPW>
+template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.best[0] = 0ull;
@@ -589,55 +596,269 @@ __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
   const int rb = row_bytes_of(RF, a.d);
   HRegs<RF, CH> hr;
   load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  for (int k0 = wg * kRPI * GPW; k0 < a.c; k0 += nw * kRPI * GPW) {
-    RowGroup<RF, CH> g[GPW];
+  for (int k0 = wg * kRPI; k0 < a.c; k0 += nw * kRPI) {
+    RowGroup<RF, CH> g;
+    rows_load<RF, CH>(g, a.C, rb, k0, a.c, nullptr, 0, lane);
+    float s[kRPI];
+    rows_dot<RF, CH>(g, hr, s);
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) rows_load<RF, CH>(g[gi], a.C, rb, k0 + gi * kRPI, a.c, nullptr, 0, lane);
-#pragma unroll
-    for (int gi = 0; gi < GPW; ++gi) {
-      float s[kRPI];
-      rows_dot<RF, CH>(g[gi], hr, s);
-#pragma unroll
-      for (int i = 0; i < kRPI; ++i) {
-        const int k = k0 + gi * kRPI + i;
-        if (lane == i && k < a.c) {
-          const float key = make_key(s[i], a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
-          a.keys[k] = key;
-          if (a.keys_out) a.keys_out[k] = key;
-        }
+    for (int i = 0; i < kRPI; ++i) {
+      const int k = k0 + i;
+      if (lane == i && k < a.c) {
+        const float key = make_key(s[i], a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
+        a.keys[k] = key;
+        if (a.keys_out) a.keys_out[k] = key;
       }
     }
   }
 }
 
-template <int RF, int CH, int NT>
+__device__ __forceinline__ int lane_prefix(uint64_t bal) {   // set bits of bal below this lane
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+struct FastScratch {
+  uint32_t wmm[2][16];          // per-wave max / min of the keys
+  int wtot[2][16];              // per-wave totals (histogram slices, bitmap words)
+  int bdig[3];                  // boundary bin, keys above it, keys in it
+  int ncand;
+  uint32_t cu[kCand];
+  int cid[kCand];
+};
+
+// Fast exact selection over register keys (ids 4 (t + j NT) + e), one histogram pass:
+// bins linear in the float key between the block min and max; each wave scans its
+// 2048 / NWAVE-bin slice from the top; the keys of the boundary bin are gathered (wave
+// ballots) and ranked by every wave with lane reads.  Returns false when the boundary bin
+// holds more than kCand keys or all keys are equal (the caller then runs select_regs).
+// Requires S.hist cleared before its first barrier.  Barriers: 4.
+template <int KV, int NWAVE>
+__device__ __forceinline__ bool select_fast(const uint32_t (&u)[KV][4], int c, int p, uint32_t vmax, uint32_t vmin,
+                                            SelShared& S, FastScratch& F, uint32_t& Tu_out, int& Tid_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NT = NWAVE * 64;
+  auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
+  vmax = wave_minmax_u32<true>(vmax);
+  vmin = wave_minmax_u32<false>(vmin);
+  if (lane == 0) { F.wmm[0][wave] = vmax; F.wmm[1][wave] = vmin; }
+  __syncthreads();                                                     // 1
+  uint32_t mx[NWAVE], mn[NWAVE];
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) { mx[w] = F.wmm[0][w]; mn[w] = F.wmm[1][w]; }
+  uint32_t ihi = mx[0], ilo = mn[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) { ihi = max(ihi, mx[w]); ilo = min(ilo, mn[w]); }
+  if (ilo == ihi) return false;                                        // all keys equal
+  const float lo_f = ord_to_float(ilo), hi_f = ord_to_float(ihi);
+  const float inv = (float)kSelBins / (hi_f - lo_f);
+  if (!(inv > 0.f && inv < 3.0e38f)) return false;
+  int bins[KV][4];
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bins[j][e] = sel_bin(u[j][e], true, lo_f, inv, ilo, 0);
+      if (idof(j, e) < c) atomicAdd(&S.hist[bins[j][e]], 1);
+    }
+  __syncthreads();                                                     // 2
+  // wave w scans bins [2048 - BPW (w+1), 2048 - BPW w) from the top, BPL per lane
+  constexpr int BPW = kSelBins / NWAVE, BPL = BPW / 64;
+  const int top = kSelBins - 1 - wave * BPW - lane * BPL;
+  int hcnt[BPL], local = 0;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) { hcnt[i] = S.hist[top - i]; local += hcnt[i]; }
+  const int incl = wave_incl_scan(local);
+  if (lane == 63) F.wtot[0][wave] = incl;
+  if (tid == 0) F.ncand = 0;
+  __syncthreads();                                                     // 3
+  int tw[NWAVE];
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) tw[w] = F.wtot[0][w];
+  int woffset = 0;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) woffset += w < wave ? tw[w] : 0;
+  // every lane finds the boundary from the wave totals and its own slice
+  int total_before_wave = 0, bw = -1;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    if (bw < 0 && total_before_wave + tw[w] >= p) bw = w;
+    if (bw < 0) total_before_wave += tw[w];
+  }
+  int b = -1, above = 0, inbin = 0;
+  {
+    const int before = woffset + incl - local;
+    int fb = -1, fa = 0, fh = 0;
+    if (wave == bw && before < p && before + local >= p) {
+      int acc = before;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        if (fb < 0 && acc + hcnt[i] >= p) { fb = top - i; fa = acc; fh = hcnt[i]; }
+        acc += hcnt[i];
+      }
+      F.bdig[0] = fb; F.bdig[1] = fa; F.bdig[2] = fh;
+    }
+  }
+  __syncthreads();                                                     // 4 (bdig)
+  b = F.bdig[0];
+  above = F.bdig[1];
+  inbin = F.bdig[2];
+  if (inbin > kCand) return false;
+  const int need_in = p - above;
+  // gather the boundary bin's keys (most waves hold none: one ballot decides)
+  uint32_t mm = 0u;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mm |= (idof(j, e) < c && bins[j][e] == b) ? (1u << (4 * j + e)) : 0u;
+  if (__ballot(mm != 0u)) {
+#pragma unroll
+    for (int j = 0; j < KV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool match = (mm >> (4 * j + e)) & 1u;
+        const uint64_t bal = __ballot(match);
+        if (bal) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&F.ncand, __popcll(bal));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (match) {
+            const int slot = base + lane_prefix(bal);
+            if (slot < kCand) { F.cu[slot] = u[j][e]; F.cid[slot] = idof(j, e); }
+          }
+        }
+      }
+  }
+  __syncthreads();                                                     // 5
+  const int n = min(F.ncand, kCand);
+  // every wave ranks the candidates (lane t holds candidate t, t + 64, ...); the
+  // need_in-th by (u desc, id asc) is the boundary
+  uint32_t tu = 0u;
+  int tb = -1;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    const uint32_t ut = t < n ? F.cu[t] : 0u;
+    const int it = t < n ? F.cid[t] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int q0 = 0; q0 < n; q0 += 64) {
+      const uint32_t uq_l = q0 + lane < n ? F.cu[q0 + lane] : 0u;
+      const int iq_l = q0 + lane < n ? F.cid[q0 + lane] : 0x7FFFFFFF;
+      const int qn = min(64, n - q0);
+      for (int q = 0; q < qn; ++q) {
+        const uint32_t uq = (uint32_t)__builtin_amdgcn_readlane((int)uq_l, q);
+        const int iq = __builtin_amdgcn_readlane(iq_l, q);
+        rank += (uq > ut) || (uq == ut && iq < it);
+      }
+    }
+    if (t < n && rank == need_in - 1) { tu = ut; tb = it; }
+  }
+  const uint64_t fb = __ballot(tb >= 0);
+  if (!fb) return false;
+  const int src = __ffsll((unsigned long long)fb) - 1;
+  Tu_out = (uint32_t)__builtin_amdgcn_readlane((int)tu, src);
+  Tid_out = __builtin_amdgcn_readlane(tb, src);
+  return true;
+}
+
+// Rank structure of the kept bitmap: wave w owns words [64 w, 64 w + 64), one per lane;
+// S.woff[word] gets the kept count of the preceding words of the same wave slice and
+// F.wtot[1][w] the slice totals.  One barrier; call with the bitmap complete.
+template <int NWAVE>
+__device__ __forceinline__ void kept_index(SelShared& S, FastScratch& F, int nwords) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int w0 = wave * 64; w0 < kMaxWords; w0 += NWAVE * 64) {
+    const int w = w0 + lane;
+    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
+    const int incl = wave_incl_scan(pc);
+    S.woff[w] = incl - pc;
+    if (lane == 63) F.wtot[1][w0 >> 6] = incl;        // slices beyond NWAVE only when c > 64 NWAVE 32
+  }
+  __syncthreads();
+}
+
+// Cluster id of ascending rank q (wave-uniform q; all lanes get it).
+template <int NWAVE>
+__device__ __forceinline__ int kept_id(const SelShared& S, const FastScratch& F, int q) {
+  const int lane = threadIdx.x & 63;
+  // slice holding rank q: slice totals live in F.wtot[1][0 .. kMaxWords / 64)
+  constexpr int NS = kMaxWords / 64;
+  const int tot = lane < NS ? F.wtot[1][lane] : 0;
+  const int incl = wave_incl_scan(tot);
+  const uint64_t in_slice = __ballot(lane < NS && incl > q);
+  const int sl = __ffsll((unsigned long long)in_slice) - 1;
+  const int sbase = __builtin_amdgcn_readlane(incl - tot, sl);
+  const int qq = q - sbase;
+  const int w = sl * 64 + lane;
+  const int off = S.woff[w];
+  const uint32_t bits = S.bitmap[w];
+  const uint64_t ok = __ballot(off <= qq && off + __popc(bits) > qq);
+  const int src = __ffsll((unsigned long long)ok) - 1;
+  int id = 0;
+  if (lane == src) {
+    uint32_t bb = bits;
+    for (int k = off; k < qq; ++k) bb &= bb - 1u;
+    id = (w << 5) + __ffs(bb) - 1;
+  }
+  return __builtin_amdgcn_readlane(id, src);
+}
+
+template <int RF, int CH, int NT, int KV>
 __global__ __launch_bounds__(NT) void k_b1_select_tiles(B1Params a) {
   constexpr int NWAVE = NT / 64;
-  constexpr int KV = 32768 / (4 * NT);
   constexpr int MAXLIST = 256;      // probes per workgroup (p <= MAXLIST * gridDim.x)
   __shared__ SelShared S;
+  __shared__ FastScratch F;
   __shared__ int my_list[MAXLIST];
   __shared__ uint64_t wmax[NWAVE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, me = blockIdx.x;
   uint32_t u[KV][4];
+  load_keys<KV>(a.keys, a.c, u, S);        // also clears S.hist and S.bitmap
+  uint32_t vmax = 0u, vmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * (tid + j * NT) + e < a.c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
   uint32_t Tu;
   int Tid;
-  load_keys<KV>(a.keys, a.c, u, S);
-  select_regs<KV>(u, a.c, a.p, S, Tu, Tid);
-  mark_kept<KV>(u, a.c, Tu, Tid, S);
-  const int nwords = (a.c + 31) >> 5;
+  bool ok = select_fast<KV, NWAVE>(u, a.c, a.p, vmax, vmin, S, F, Tu, Tid);
+  if (!ok) {                                // wide boundary bin or equal keys: the general select
+    __syncthreads();
+    for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
+    __syncthreads();
+    select_regs<KV>(u, a.c, a.p, S, Tu, Tid);
+  }
+  // mark the kept set
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int id0 = 4 * (tid + j * NT);
+    uint32_t m = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int id = id0 + e;
+      m |= (id < a.c && (u[j][e] > Tu || (u[j][e] == Tu && id <= Tid))) ? (1u << e) : 0u;
+    }
+    if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
+  }
+  __syncthreads();
+  kept_index<NWAVE>(S, F, (a.c + 31) >> 5);
   const int n_my = me < a.p ? (a.p - me + G - 1) / G : 0;
-  for (int i = tid; i < n_my; i += NT) my_list[i] = kept_at(S, nwords, me + i * G);
+  for (int i = wave; i < n_my; i += NWAVE) {
+    const int k = kept_id<NWAVE>(S, F, me + i * G);
+    if (lane == 0) my_list[i] = k;
+  }
   if (me == 0 && a.probe_out)
-    for (int q = tid; q < a.p; q += NT) a.probe_out[q] = kept_at(S, nwords, q);
+    for (int q = wave; q < a.p; q += NWAVE) {
+      const int k = kept_id<NWAVE>(S, F, q);
+      if (lane == 0) a.probe_out[q] = k;
+    }
   __syncthreads();
   // stage 2 on this workgroup's probes
+  HRegs<RF, CH> hr;
+  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
   const int ngroups = (a.b + kRPI - 1) / kRPI;
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
-  HRegs<RF, CH> hr;
-  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
   uint64_t bc = 0;
   for (int it = wave; it < n_my * ngroups; it += NWAVE) {
     const int qi = it / ngroups, j0 = (it % ngroups) * kRPI;
@@ -1014,6 +1235,7 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   off = up(off + (size_t)B * sizeof(uint64_t));
   w.done = (uint32_t*)(b ? b + off : nullptr);
   off = up(off + 4 * sizeof(uint32_t));
+
   w.probes = (int32_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * p * sizeof(int32_t));
   w.bytes = off;
@@ -1053,10 +1275,9 @@ int chunk_slots(int fmt, int d) {
 
 template <int RF, int CH>
 static void launch_b1_scores(const B1Params& a, int c, hipStream_t st) {
-  constexpr int GPW = CH <= 4 ? 2 : 1;
-  const int groups = (c + kRPI - 1) / kRPI;
-  const int wgs = (groups + 4 * GPW - 1) / (4 * GPW);
-  hipLaunchKernelGGL((k_b1_scores<RF, CH, GPW>), dim3(wgs), dim3(kThreads), 0, st, a);
+  const int groups = (c + kRPI - 1) / kRPI;          // one row group per wave
+  const int wgs = (groups + 3) / 4;
+  hipLaunchKernelGGL((k_b1_scores<RF, CH>), dim3(wgs), dim3(kThreads), 0, st, a);
 }
 
 template <int RF, int CH>
@@ -1064,7 +1285,15 @@ static void launch_b1_pair(const B1Params& a, int c, int p, hipStream_t st) {
   launch_b1_scores<RF, CH>(a, c, st);
   int G = p < kB1Workgroups ? p : kB1Workgroups;
   if (G < (p + 255) / 256) G = (p + 255) / 256;
-  hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads>), dim3(G), dim3(kB1Threads), 0, st, a);
+  const int kv = (c + 4 * kB1Threads - 1) / (4 * kB1Threads);   // uint4 of keys per thread
+  if (kv <= 1)
+    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
+  else if (kv <= 2)
+    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
+  else if (kv <= 4)
+    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 4>), dim3(G), dim3(kB1Threads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 8>), dim3(G), dim3(kB1Threads), 0, st, a);
 }
 
 static bool use_mfma(const HeadShape& s, int fmt) {
