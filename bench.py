@@ -8,9 +8,11 @@ synthetic head of workloads.py with the stored balanced clustering of that head
 (tests/golden/clusters_gemma.npz); centroids and tiles are built on the GPU by the library.
 
 A step is one flashhead_forward call (centroid scores, probe selection, probe logits, token)
-over one hidden state.  Calls are captured in a HIP graph that cycles through R copies of
-(centroids, tiles, h) whose footprint is well above the 256 MB last-level cache, so every call
-reads its bytes from HBM.  Prints one JSON line.
+over one hidden state.  Calls are captured in a HIP graph that cycles through R copies of the
+centroids and R distinct hidden states over the one tile array, as a decode loop does: every
+call reads the centroids from HBM (R x 37.7 MB is well above the 256 MB last-level cache) and
+its own probe set's tiles (R different probe sets touch ~R x 19 MB of the 604 MB tiles).
+Prints one JSON line.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma] [--mode greedy]
 """
@@ -126,15 +128,15 @@ def main() -> int:
     hd = workloads.make_head(wl)
     dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.dtype, wl.e_pack, wl.dtype,
                                    device="cuda", keep_dense=not args.no_dense)
-    h0 = to_device(hd.h, "cuda")
     c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, wl.B)
-    set_bytes = dev.C.numel() * dev.C.element_size() + dev.tiles.numel() + h0.numel() * 2
     R = args.rotate or max(2, int(np.ceil(4 * MALL_BYTES / max(alg_bytes, 1))))
-    log(f"rotating {R} copies of (centroids, tiles, h): {R * set_bytes / 2**30:.1f} GiB")
+    log(f"rotating {R} copies of the centroids ({R * dev.C.numel() * dev.C.element_size() / 2**30:.2f} GiB) "
+        f"and {R} hidden states over one tile array ({dev.tiles.numel() / 2**30:.2f} GiB)")
     Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
-    Ts = [dev.tiles] + [dev.tiles.clone() for _ in range(R - 1)]
-    Ss = [dev.scales] + ([dev.scales.clone() for _ in range(R - 1)] if dev.scales is not None else [None] * (R - 1))
-    Hs = [h0] + [h0.clone() for _ in range(R - 1)]
+    Ts = [dev.tiles] * R
+    Ss = [dev.scales] * R
+    Hs = [to_device(hd.h, "cuda")] + [to_device(workloads.make_hidden(wl, wl.B, seed=1000 + r), "cuda")
+                                      for r in range(1, R)]
     B, p = wl.B, wl.p
     desc = dev.desc(B)
     ws = dev.workspace(B, p)

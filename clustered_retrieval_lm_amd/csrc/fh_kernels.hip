@@ -891,14 +891,7 @@ __global__ __launch_bounds__(NT) void k_b1_select_tiles(B1Params a) {
   if (tid == 0) {
     uint64_t m = wmax[0];
     for (int w = 1; w < NWAVE; ++w) m = wmax[w] > m ? wmax[w] : m;
-    if (m) atomicMax((unsigned long long*)a.best, (unsigned long long)m);
-    __threadfence();
-    const uint32_t prev = atomicAdd(a.done, 1u);
-    if (prev == (uint32_t)G - 1) {
-      __threadfence();
-      const uint64_t fin = atomicAdd((unsigned long long*)a.best, 0ull);
-      a.token[0] = (int32_t)cand_id(fin);
-    }
+    if (m) atomicMax((unsigned long long*)a.best, (unsigned long long)m);   // k_finalize decodes it
   }
 }
 
@@ -1294,6 +1287,7 @@ static void launch_b1_pair(const B1Params& a, int c, int p, hipStream_t st) {
     hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 4>), dim3(G), dim3(kB1Threads), 0, st, a);
   else
     hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 8>), dim3(G), dim3(kB1Threads), 0, st, a);
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, (const uint64_t*)a.best, a.token, 1);
 }
 
 static bool use_mfma(const HeadShape& s, int fmt) {
