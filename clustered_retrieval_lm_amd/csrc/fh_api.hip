@@ -223,6 +223,40 @@ fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h, 
   return FH_OK;
 }
 
+// Probe selection and stage 2: at B = 1 one fused kernel, else the select and tile kernels.
+static fh_status select_and_probe(const fh::HeadShape& s, int p, const void* h, const int32_t* c2t,
+                                  const void* tiles, const void* scales, const fh::Sampling& smp,
+                                  const fh::Workspace& ws, const fh_outputs* out, hipStream_t hs) {
+  hipError_t e;
+  if (s.B == 1) {
+    e = fh::launch_stage2_b1(s, p, h, c2t, tiles, (const uint16_t*)scales, smp, ws, out->probe_ids,
+                             out->probe_logits, out->probe_tokens, out->token, hs);
+    if (e != hipSuccess) return hip_fail(e, "fused selection and probe logits launch");
+    return FH_OK;
+  }
+  e = fh::launch_select(s, p, ws, out->probe_ids, hs);
+  if (e != hipSuccess) return hip_fail(e, "probe selection launch");
+  e = fh::launch_tiles(s, p, h, c2t, tiles, (const uint16_t*)scales, smp, ws, out->probe_logits, out->probe_tokens,
+                       out->token, hs);
+  if (e != hipSuccess) return hip_fail(e, "probe logits launch");
+  return FH_OK;
+}
+
+fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void* h, const int32_t* cluster_tokens,
+                                     const void* E_tiles, const void* E_scales, int32_t mode, float temperature,
+                                     uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                                     const fh_outputs* out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if ((st = check_tiles_args(desc, h, cluster_tokens, E_tiles, E_scales, out)) != FH_OK) return st;
+  fh::Workspace ws;
+  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  return select_and_probe(shape_of(desc), (int)p, h, cluster_tokens, E_tiles, E_scales,
+                          sampling_of(mode, temperature, seed, step), ws, out, (hipStream_t)stream);
+}
+
 fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
                             const void* E_tiles, const void* E_scales, int64_t p, int32_t mode, float temperature,
                             uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
@@ -238,20 +272,9 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
   const fh::HeadShape s = shape_of(desc);
   const fh::Sampling smp = sampling_of(mode, temperature, seed, step);
   hipStream_t hs = (hipStream_t)stream;
-  if (s.B == 1 && s.c_fmt == s.e_fmt) {
-    hipError_t e = fh::launch_forward_b1(s, (int)p, h, centroids, cluster_tokens, E_tiles, (const uint16_t*)E_scales,
-                                         smp, ws, out->probe_ids, out->probe_logits, out->probe_tokens, out->token, hs);
-    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
-    return FH_OK;
-  }
   hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
-  e = fh::launch_select(s, (int)p, ws, out->probe_ids, hs);
-  if (e != hipSuccess) return hip_fail(e, "probe selection launch");
-  e = fh::launch_tiles(s, (int)p, h, cluster_tokens, E_tiles, (const uint16_t*)E_scales, smp, ws, out->probe_logits,
-                       out->probe_tokens, out->token, hs);
-  if (e != hipSuccess) return hip_fail(e, "probe logits launch");
-  return FH_OK;
+  return select_and_probe(s, (int)p, h, cluster_tokens, E_tiles, E_scales, smp, ws, out, hs);
 }
 
 fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes) {

@@ -28,7 +28,6 @@ struct Workspace {
   float* keys;        // [B][c] stage-1 keys
   int32_t* probes;    // [B][p] kept clusters, ascending
   uint64_t* best;     // [B] packed (key, ~token) maxima
-  uint32_t* done;     // [4] completion counters of the fused B = 1 path
   uint64_t* mask;     // [c][W] rows that kept cluster k (B > 1 only), W = ceil(B / 64)
   int W;
   size_t bytes;
@@ -49,12 +48,11 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
                         const void* tiles, const uint16_t* scales, const Sampling& smp,
                         const Workspace& ws, float* logits_out, int32_t* tokens_out,
                         int32_t* token, hipStream_t st);
-// Fused B = 1 forward (two kernels); hipErrorNotSupported if the centroid and tile row
-// formats differ, in which case the caller uses the staged kernels.
-hipError_t launch_forward_b1(const HeadShape& s, int p, const void* h, const void* C, const int32_t* c2t,
-                             const void* tiles, const uint16_t* scales, const Sampling& smp, const Workspace& ws,
-                             int32_t* probe_out, float* logits_out, int32_t* tokens_out, int32_t* token,
-                             hipStream_t st);
+// B = 1 probe selection fused with stage 2 (one kernel, then the token decode); reads the
+// keys launch_scores left in the workspace.
+hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int32_t* c2t, const void* tiles,
+                            const uint16_t* scales, const Sampling& smp, const Workspace& ws, int32_t* probe_out,
+                            float* logits_out, int32_t* tokens_out, int32_t* token, hipStream_t st);
 hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E, const Sampling& smp,
                         uint64_t* best, int32_t* token, float* logits, hipStream_t st);
 hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int unit, const void* E,

@@ -574,7 +574,6 @@ struct B1Params {
   float* keys;
   float* keys_out;      // optional copy of the keys (staged entry point)
   uint64_t* best;
-  uint32_t* done;
   const int32_t* c2t;
   const char* tiles;
   const uint16_t* scales;
@@ -588,7 +587,6 @@ template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.best[0] = 0ull;
-    a.done[0] = 0u;
   }
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -1015,9 +1013,14 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   }
 }
 
-__global__ void k_finalize(const uint64_t* best, int32_t* token, int B) {
+// Decodes the per-row maxima and clears them, so the workspace holds zero maxima
+// between calls.
+__global__ void k_finalize(uint64_t* best, int32_t* token, int B) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) token[i] = (int32_t)cand_id(best[i]);
+  if (i < B) {
+    token[i] = (int32_t)cand_id(best[i]);
+    best[i] = 0ull;
+  }
 }
 
 __global__ void k_fill_u64(uint64_t* p, int n, uint64_t v) {
@@ -1226,9 +1229,6 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   }
   w.best = (uint64_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * sizeof(uint64_t));
-  w.done = (uint32_t*)(b ? b + off : nullptr);
-  off = up(off + 4 * sizeof(uint32_t));
-
   w.probes = (int32_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * p * sizeof(int32_t));
   w.bytes = off;
@@ -1274,8 +1274,7 @@ static void launch_b1_scores(const B1Params& a, int c, hipStream_t st) {
 }
 
 template <int RF, int CH>
-static void launch_b1_pair(const B1Params& a, int c, int p, hipStream_t st) {
-  launch_b1_scores<RF, CH>(a, c, st);
+static void launch_b1_stage2(const B1Params& a, int c, int p, hipStream_t st) {
   int G = p < kB1Workgroups ? p : kB1Workgroups;
   if (G < (p + 255) / 256) G = (p + 255) / 256;
   const int kv = (c + 4 * kB1Threads - 1) / (4 * kB1Threads);   // uint4 of keys per thread
@@ -1287,7 +1286,7 @@ static void launch_b1_pair(const B1Params& a, int c, int p, hipStream_t st) {
     hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 4>), dim3(G), dim3(kB1Threads), 0, st, a);
   else
     hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 8>), dim3(G), dim3(kB1Threads), 0, st, a);
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, (const uint64_t*)a.best, a.token, 1);
+  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, a.best, a.token, 1);
 }
 
 static bool use_mfma(const HeadShape& s, int fmt) {
@@ -1321,7 +1320,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     B1Params a{};
     a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
     a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
-    a.keys = ws.keys; a.keys_out = keys_out; a.best = ws.best; a.done = ws.done;
+    a.keys = ws.keys; a.keys_out = keys_out; a.best = ws.best;
     const int ch = chunk_slots(s.c_fmt, s.d);
     if (s.c_fmt == RF_F32) {
       FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
@@ -1384,29 +1383,26 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, (const uint64_t*)ws.best, token, s.B);
+  hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, ws.best, token, s.B);
   return hipGetLastError();
 }
 
-hipError_t launch_forward_b1(const HeadShape& s, int p, const void* h, const void* C, const int32_t* c2t,
-                             const void* tiles, const uint16_t* scales, const Sampling& smp, const Workspace& ws,
-                             int32_t* probe_out, float* logits_out, int32_t* tokens_out, int32_t* token,
-                             hipStream_t st) {
+hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int32_t* c2t, const void* tiles,
+                            const uint16_t* scales, const Sampling& smp, const Workspace& ws, int32_t* probe_out,
+                            float* logits_out, int32_t* tokens_out, int32_t* token, hipStream_t st) {
   B1Params a{};
-  a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
+  a.h = h; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
   a.sample = smp.sample; a.tau = smp.tau; a.rng = make_rng(smp.seed, smp.step);
-  a.keys = ws.keys; a.best = ws.best; a.done = ws.done;
+  a.keys = ws.keys; a.best = ws.best;
   a.c2t = c2t; a.tiles = (const char*)tiles; a.scales = scales;
   a.probe_out = probe_out; a.logits_out = logits_out; a.tokens_out = tokens_out; a.token = token;
-  // the centroid rows and the tile rows may differ in format: dispatch on the pair
-  const int chc = chunk_slots(s.c_fmt, s.d), che = chunk_slots(s.e_fmt, s.d);
-  if (s.c_fmt != s.e_fmt || chc != che) return hipErrorNotSupported;
+  const int ch = chunk_slots(s.e_fmt, s.d);
   if (s.e_fmt == RF_F32) {
-    FH_DISPATCH_CH(che, (launch_b1_pair<RF_F32, kCH>(a, s.c, p, st)));
+    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_F32, kCH>(a, s.c, p, st)));
   } else if (s.e_fmt == RF_BF16) {
-    FH_DISPATCH_CH(che, (launch_b1_pair<RF_BF16, kCH>(a, s.c, p, st)));
+    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_BF16, kCH>(a, s.c, p, st)));
   } else {
-    return hipErrorNotSupported;
+    FH_DISPATCH_CH_INT4(ch, (launch_b1_stage2<RF_INT4, kCH>(a, s.c, p, st)));
   }
   return hipGetLastError();
 }
@@ -1439,7 +1435,7 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, (const uint64_t*)best, token, s.B);
+  hipLaunchKernelGGL(k_finalize, dim3((s.B + 255) / 256), dim3(256), 0, st, best, token, s.B);
   return hipGetLastError();
 }
 

@@ -68,6 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_centroid_scores": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_select_probes": ([D, i64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_probe_logits": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
+        "flashhead_select_and_probe": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
         "flashhead_forward": ([D, vp, vp, vp, vp, vp, i64, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
         "flashhead_dense_workspace_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_dense_forward": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp, vp], ctypes.c_int),
@@ -176,6 +177,14 @@ def flashhead_select_probes(desc: fh_desc, p, workspace, probe_ids_out=None, str
 def flashhead_probe_logits(desc: fh_desc, p, h, cluster_tokens, E_tiles, E_scales, mode, temperature, seed,
                            step, workspace, out: fh_outputs, stream=None) -> None:
     _check(load_library().flashhead_probe_logits(
+        ctypes.byref(desc), int(p), _ptr(h), _ptr(cluster_tokens), _ptr(E_tiles), _ptr(E_scales), _mode(mode),
+        float(temperature), int(seed), int(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(out), _stream(stream)))
+
+
+def flashhead_select_and_probe(desc: fh_desc, p, h, cluster_tokens, E_tiles, E_scales, mode, temperature, seed,
+                               step, workspace, out: fh_outputs, stream=None) -> None:
+    _check(load_library().flashhead_select_and_probe(
         ctypes.byref(desc), int(p), _ptr(h), _ptr(cluster_tokens), _ptr(E_tiles), _ptr(E_scales), _mode(mode),
         float(temperature), int(seed), int(step), _ptr(workspace), workspace.numel() * workspace.element_size(),
         ctypes.byref(out), _stream(stream)))

@@ -97,8 +97,8 @@ const char* flashhead_version(void);
 const char* flashhead_last_error(void);
 
 /*
- * Workspace size (bytes, device memory) that flashhead_forward and the three stage entry
- * points need for this desc and p.  Writes it to *bytes (host).  The workspace carries
+ * Workspace size (bytes, device memory) that flashhead_forward and the stage entry points
+ * need for this desc and p.  Writes it to *bytes (host).  The workspace carries
  * the centroid keys, probe lists and per-row maxima between the stages of one call; it
  * needs no initialisation.
  */
@@ -177,7 +177,22 @@ fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h,
                                  size_t workspace_bytes, const fh_outputs* out, void* stream);
 
 /*
- * The whole head: stage 1, probe selection and stage 2 as above, enqueued back to back.
+ * Probe selection and stage 2 in one call: the same results as flashhead_select_probes
+ * followed by flashhead_probe_logits (out->probe_ids receives the kept ids, ascending, if
+ * non-NULL).  Reads the keys the last flashhead_centroid_scores call left in `workspace`, so
+ * flashhead_centroid_scores + flashhead_select_and_probe is flashhead_forward.  At B = 1 the
+ * selection and the probed logits run in one kernel: every workgroup selects the same kept
+ * set and scores its share of it.  Arguments as for flashhead_probe_logits.
+ */
+fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void* h,
+                                     const int32_t* cluster_tokens, const void* E_tiles,
+                                     const void* E_scales, int32_t mode, float temperature,
+                                     uint64_t seed, uint64_t step, void* workspace,
+                                     size_t workspace_bytes, const fh_outputs* out, void* stream);
+
+/*
+ * The whole head: stage 1, probe selection and stage 2 as above, enqueued back to back
+ * (flashhead_centroid_scores, then flashhead_select_and_probe).
  *   h              device [B][d]
  *   centroids      device [c][d]
  *   cluster_tokens device int32 [c][b]

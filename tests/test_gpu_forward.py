@@ -36,8 +36,15 @@ def _run_and_compare(dev: DeviceHead, hd_h: np.ndarray, h_dtype: str, C, C2T, ti
     o2 = dev.outputs(B, p)
     fh.flashhead_probe_logits(desc, p, h, dev.c2t, dev.tiles, dev.scales, mode, tau, seed, step, ws,
                               fh.make_outputs(o2["token"], None, o2["probe_logits"], o2["probe_tokens"]))
+    # stage 1 then selection + stage 2 in one call (the two halves of flashhead_forward)
+    o3 = dev.outputs(B, p)
+    fh.flashhead_select_and_probe(desc, p, h, dev.c2t, dev.tiles, dev.scales, mode, tau, seed, step, ws,
+                                  fh.make_outputs(o3["token"], o3["probe_ids"], o3["probe_logits"],
+                                                  o3["probe_tokens"]))
     torch.cuda.synchronize()
     got = {k: v.cpu().numpy() for k, v in out.items()}
+    for k, v in o3.items():
+        assert np.array_equal(v.cpu().numpy(), got[k]), f"select_and_probe and forward differ in {k}"
     assert np.array_equal(ids2.cpu().numpy(), got["probe_ids"]), "staged and fused probe ids differ"
     assert np.array_equal(o2["token"].cpu().numpy(), got["token"]), "staged and fused tokens differ"
     assert np.array_equal(o2["probe_logits"].cpu().numpy(), got["probe_logits"])
