@@ -44,6 +44,45 @@ def algorithmic_bytes(wl, B=1):
     return c_bytes, tile_bytes, c_bytes + tile_bytes + B * wl.d * csz
 
 
+def source_sha256() -> str:
+    """sha256 over the library sources, the key under which counter results are stored."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "clustered_retrieval_lm_amd", "csrc", "*"))):
+        with open(f, "rb") as fh_:
+            h.update(fh_.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernels) -> "int | None":
+    """HBM bytes per launch of `kernels` (name prefixes) from profiles/hbm_traffic_<workload>_b1.txt.
+
+    That file holds FETCH_SIZE / WRITE_SIZE per dispatch from two rocprofv3 --pmc runs of
+    this script, scaled by the factors a plain 1 GiB copy gave.  None when it is missing or
+    was taken on other library sources than the ones built now.
+    """
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_b1.txt")
+    if not os.path.exists(path):
+        return None
+    sha, found = None, {}
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif line.startswith("kernel:"):
+            f = line.split()
+            found[f[1]] = int(f[-1].split("=")[1])
+    if sha != source_sha256():
+        return None
+    total = 0
+    for k in kernels:
+        hits = [v for n, v in found.items() if n.split("<")[0] == k]
+        if len(hits) != 1:
+            return None
+        total += hits[0]
+    return total
+
+
 def time_graph(torch, launch, n_calls, reps, warm_reps=2):
     """Capture n_calls launches in one graph; return seconds per call over `reps` replays."""
     s = torch.cuda.Stream()
@@ -178,7 +217,7 @@ def main() -> int:
     del g_fwd
 
     # ---- the two halves of a call, each timed alone the same way: stage 1 (k_b1_scores) and
-    # selection + stage 2 (k_b1_select_tiles + the one-block token decode), the latter over R
+    # selection + stage 2 (k_b1_stage2 + the one-block token decode), the latter over R
     # workspaces that hold the stage-1 keys of the R hidden states
     t_sc, g_sc = time_graph(torch, scores, G, reps, warm_reps=1)
     sc_bytes = c_bytes + B * wl.d * 2 + B * wl.c * 4
@@ -247,12 +286,14 @@ def main() -> int:
         log(f"oracle: {cpu['value']:.2f} calls/s on {cpu['cores']} threads")
 
     units = {
-        "k_b1_scores (centroid scores)": (sc_bytes, t_sc),
-        "k_b1_select_tiles + k_finalize (selection, probe logits, token)": (s2_bytes, t_s2),
+        "k_b1_scores (centroid scores)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
+        "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
+            (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
     }
     dom = max(units, key=lambda k: units[k][1])
-    dom_bytes, dom_t = units[dom]
+    dom_bytes, dom_t, dom_kernels = units[dom]
     dom_gbs = dom_bytes / dom_t / 1e9
+    traffic = measured_traffic(args.workload, dom_kernels) if args.mode == "greedy" else None
     res = {
         "metric": "head calls/s + achieved HBM GB/s vs dense LM head, B=1 Gemma-3-1B shape",
         "value": round(calls_per_s, 1),
@@ -273,10 +314,10 @@ def main() -> int:
         "algorithmic_bytes": alg_bytes,
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_t * 1e6, 3)},
         "kernels": {k: {"bytes_per_launch": b_, "us_per_launch": round(t_ * 1e6, 3),
-                        "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_) in units.items()},
+                        "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_, _) in units.items()},
         "dense": dense,
         "cpu_baseline": cpu,
     }

@@ -78,10 +78,12 @@ __device__ __forceinline__ float word_to_uniform(uint32_t w) {
 __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 
 // Probe or token key: the logit itself (greedy) or logit / tau + Gumbel noise (sampling).
+// Adding +0 turns a -0 key into +0 (round to nearest), so keys compare the same as floats
+// and as ord_key values.
 __device__ __forceinline__ float make_key(float z, int sample, float tau, const Rng& g, uint32_t row,
                                           uint32_t stream, uint32_t n) {
-  if (!sample) return z;
-  return z / tau + gumbel(word_to_uniform(rng_word(g, row, stream, n)));
+  if (!sample) return z + 0.0f;
+  return z / tau + gumbel(word_to_uniform(rng_word(g, row, stream, n))) + 0.0f;
 }
 
 // ---------------------------------------------------------------- wave reductions
@@ -131,6 +133,20 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
   v = op(v, (uint32_t)dpp_i<0x142, 0xA, false>(id, (int)v));
   v = op(v, (uint32_t)dpp_i<0x143, 0xC, false>(id, (int)v));
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Max / min of floats over the 64 lanes (NaN-free inputs), returned wave-uniform.
+template <bool MAX>
+__device__ __forceinline__ float wave_minmax_f32(float v) {
+  const int id = (int)(MAX ? 0xFF800000u : 0x7F800000u);    // -inf / +inf
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  v = op(v, __int_as_float(dpp_i<0xB1, 0xF, false>(id, __float_as_int(v))));
+  v = op(v, __int_as_float(dpp_i<0x4E, 0xF, false>(id, __float_as_int(v))));
+  v = op(v, __int_as_float(dpp_i<0x141, 0xF, false>(id, __float_as_int(v))));
+  v = op(v, __int_as_float(dpp_i<0x140, 0xF, false>(id, __float_as_int(v))));
+  v = op(v, __int_as_float(dpp_i<0x142, 0xA, false>(id, __float_as_int(v))));
+  v = op(v, __int_as_float(dpp_i<0x143, 0xC, false>(id, __float_as_int(v))));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {

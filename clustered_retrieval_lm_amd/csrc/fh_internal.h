@@ -28,6 +28,7 @@ struct Workspace {
   float* keys;        // [B][c] stage-1 keys
   int32_t* probes;    // [B][p] kept clusters, ascending
   uint64_t* best;     // [B] packed (key, ~token) maxima
+  uint64_t* part;     // [256] per-workgroup maxima of the fused B = 1 stage 2
   uint64_t* mask;     // [c][W] rows that kept cluster k (B > 1 only), W = ceil(B / 64)
   int W;
   size_t bytes;

@@ -38,19 +38,19 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 
 // ------------------------------------------------------------------ row dot products
 
-template <int RF, int CH>
+template <int RF, int CH, int NR = kRPI>
 struct RowGroup {
-  uint4 w[kRPI][CH];
-  float sc[kRPI][CH];
+  uint4 w[NR][CH];
+  float sc[NR][CH];
 };
 
-// Load rows [j0, j0 + kRPI) (those < nrows) of a matrix with row stride rb bytes.
-template <int RF, int CH>
-__device__ __forceinline__ void rows_load(RowGroup<RF, CH>& g, const char* base, int rb, int j0, int nrows,
+// Load rows [j0, j0 + NR) (those < nrows) of a matrix with row stride rb bytes.
+template <int RF, int CH, int NR>
+__device__ __forceinline__ void rows_load(RowGroup<RF, CH, NR>& g, const char* base, int rb, int j0, int nrows,
                                           const uint16_t* scales, int spr, int lane) {
   const int cpr = rb >> 4;
 #pragma unroll
-  for (int r = 0; r < kRPI; ++r) {
+  for (int r = 0; r < NR; ++r) {
     const int j = j0 + r;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -63,10 +63,10 @@ __device__ __forceinline__ void rows_load(RowGroup<RF, CH>& g, const char* base,
 }
 
 // Full dot products of the loaded rows with h (every lane receives every sum).
-template <int RF, int CH>
-__device__ __forceinline__ void rows_dot(const RowGroup<RF, CH>& g, const HRegs<RF, CH>& hr, float (&out)[kRPI]) {
+template <int RF, int CH, int NR>
+__device__ __forceinline__ void rows_dot(const RowGroup<RF, CH, NR>& g, const HRegs<RF, CH>& hr, float (&out)[NR]) {
 #pragma unroll
-  for (int r = 0; r < kRPI; ++r) {
+  for (int r = 0; r < NR; ++r) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) acc = chunk_dot<RF>(g.w[r][i], hr.v[i], acc, g.sc[r][i]);
@@ -557,12 +557,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
 }
 
 // ------------------------------------------------------------------ B = 1 fused path
-// Two kernels per call.  k_b1_scores streams C (one 4-row group per wave, all row loads
-// issued before any arithmetic) and writes the keys; its block 0 clears the per-call state
-// of the second kernel.  k_b1_select_tiles: every workgroup loads the c keys into registers
-// and runs the same exact top-p selection (select_fast), keeps the probes whose rank q
-// satisfies q % gridDim.x == blockIdx.x, streams their tiles, and the last workgroup to
-// finish writes the token.  No workgroup ever waits for another.
+// Three kernels per call.  k_b1_scores streams C (one 4-row group per wave, all row loads
+// issued before any arithmetic) and writes the keys.  k_b1_stage2: every workgroup finds
+// the same kept set from the keys, scores its share of the kept clusters' tiles and writes
+// its best candidate; k_finalize_parts reduces those to the token.  No workgroup ever
+// waits for another.
 
 struct B1Params {
   const void* h;
@@ -573,7 +572,7 @@ struct B1Params {
   Rng rng;
   float* keys;
   float* keys_out;      // optional copy of the keys (staged entry point)
-  uint64_t* best;
+  uint64_t* part;       // [gridDim.x] per-workgroup maxima of k_b1_stage2
   const int32_t* c2t;
   const char* tiles;
   const uint16_t* scales;
@@ -585,9 +584,6 @@ struct B1Params {
 
 template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.best[0] = 0ull;
-  }
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
@@ -615,281 +611,296 @@ __device__ __forceinline__ int lane_prefix(uint64_t bal) {   // set bits of bal 
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
-struct FastScratch {
-  uint32_t wmm[2][16];          // per-wave max / min of the keys
-  int wtot[2][16];              // per-wave totals (histogram slices, bitmap words)
-  int bdig[3];                  // boundary bin, keys above it, keys in it
-  int ncand;
-  uint32_t cu[kCand];
-  int cid[kCand];
+// Shared state of k_b1_stage2.  Keys live in registers: slot s of thread t holds the key of
+// cluster s * 1024 + t, so one wave ballot covers 64 consecutive clusters and the kept set
+// is written as 64-bit words without atomics.
+constexpr int kS2Cap = 16;                 // boundary-bin keys one wave may contribute
+constexpr int kS2MaxWords = 32768 / 64;
+
+struct S2Shared {
+  int hist[kSelBins];
+  uint64_t words[kS2MaxWords];             // bit i of word w: cluster 64 w + i is kept
+  int pref[kS2MaxWords];                   // kept clusters before word w (probe id output)
+  float wmx[16], wmn[16];
+  int wtot[16];
+  int ccnt[16];
+  float cx[16][kS2Cap];
+  int cid[16][kS2Cap];
+  uint64_t wmax[16];
 };
 
-// Fast exact selection over register keys (ids 4 (t + j NT) + e), one histogram pass:
-// bins linear in the float key between the block min and max; each wave scans its
-// 2048 / NWAVE-bin slice from the top; the keys of the boundary bin are gathered (wave
-// ballots) and ranked by every wave with lane reads.  Returns false when the boundary bin
-// holds more than kCand keys or all keys are equal (the caller then runs select_regs).
-// Requires S.hist cleared before its first barrier.  Barriers: 4.
-template <int KV, int NWAVE>
-__device__ __forceinline__ bool select_fast(const uint32_t (&u)[KV][4], int c, int p, uint32_t vmax, uint32_t vmin,
-                                            SelShared& S, FastScratch& F, uint32_t& Tu_out, int& Tid_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NT = NWAVE * 64;
-  auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
-  vmax = wave_minmax_u32<true>(vmax);
-  vmin = wave_minmax_u32<false>(vmin);
-  if (lane == 0) { F.wmm[0][wave] = vmax; F.wmm[1][wave] = vmin; }
-  __syncthreads();                                                     // 1
-  uint32_t mx[NWAVE], mn[NWAVE];
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) { mx[w] = F.wmm[0][w]; mn[w] = F.wmm[1][w]; }
-  uint32_t ihi = mx[0], ilo = mn[0];
-#pragma unroll
-  for (int w = 1; w < NWAVE; ++w) { ihi = max(ihi, mx[w]); ilo = min(ilo, mn[w]); }
-  if (ilo == ihi) return false;                                        // all keys equal
-  const float lo_f = ord_to_float(ilo), hi_f = ord_to_float(ihi);
-  const float inv = (float)kSelBins / (hi_f - lo_f);
-  if (!(inv > 0.f && inv < 3.0e38f)) return false;
-  int bins[KV][4];
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      bins[j][e] = sel_bin(u[j][e], true, lo_f, inv, ilo, 0);
-      if (idof(j, e) < c) atomicAdd(&S.hist[bins[j][e]], 1);
-    }
-  __syncthreads();                                                     // 2
-  // wave w scans bins [2048 - BPW (w+1), 2048 - BPW w) from the top, BPL per lane
-  constexpr int BPW = kSelBins / NWAVE, BPL = BPW / 64;
-  const int top = kSelBins - 1 - wave * BPW - lane * BPL;
-  int hcnt[BPL], local = 0;
-#pragma unroll
-  for (int i = 0; i < BPL; ++i) { hcnt[i] = S.hist[top - i]; local += hcnt[i]; }
-  const int incl = wave_incl_scan(local);
-  if (lane == 63) F.wtot[0][wave] = incl;
-  if (tid == 0) F.ncand = 0;
-  __syncthreads();                                                     // 3
-  int tw[NWAVE];
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) tw[w] = F.wtot[0][w];
-  int woffset = 0;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) woffset += w < wave ? tw[w] : 0;
-  // every lane finds the boundary from the wave totals and its own slice
-  int total_before_wave = 0, bw = -1;
-#pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    if (bw < 0 && total_before_wave + tw[w] >= p) bw = w;
-    if (bw < 0) total_before_wave += tw[w];
-  }
-  int b = -1, above = 0, inbin = 0;
-  {
-    const int before = woffset + incl - local;
-    int fb = -1, fa = 0, fh = 0;
-    if (wave == bw && before < p && before + local >= p) {
-      int acc = before;
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        if (fb < 0 && acc + hcnt[i] >= p) { fb = top - i; fa = acc; fh = hcnt[i]; }
-        acc += hcnt[i];
-      }
-      F.bdig[0] = fb; F.bdig[1] = fa; F.bdig[2] = fh;
-    }
-  }
-  __syncthreads();                                                     // 4 (bdig)
-  b = F.bdig[0];
-  above = F.bdig[1];
-  inbin = F.bdig[2];
-  if (inbin > kCand) return false;
-  const int need_in = p - above;
-  // gather the boundary bin's keys (most waves hold none: one ballot decides)
-  uint32_t mm = 0u;
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) mm |= (idof(j, e) < c && bins[j][e] == b) ? (1u << (4 * j + e)) : 0u;
-  if (__ballot(mm != 0u)) {
-#pragma unroll
-    for (int j = 0; j < KV; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool match = (mm >> (4 * j + e)) & 1u;
-        const uint64_t bal = __ballot(match);
-        if (bal) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&F.ncand, __popcll(bal));
-          base = __builtin_amdgcn_readfirstlane(base);
-          if (match) {
-            const int slot = base + lane_prefix(bal);
-            if (slot < kCand) { F.cu[slot] = u[j][e]; F.cid[slot] = idof(j, e); }
-          }
-        }
-      }
-  }
-  __syncthreads();                                                     // 5
-  const int n = min(F.ncand, kCand);
-  // every wave ranks the candidates (lane t holds candidate t, t + 64, ...); the
-  // need_in-th by (u desc, id asc) is the boundary
-  uint32_t tu = 0u;
-  int tb = -1;
-  for (int t0 = 0; t0 < n; t0 += 64) {
-    const int t = t0 + lane;
-    const uint32_t ut = t < n ? F.cu[t] : 0u;
-    const int it = t < n ? F.cid[t] : 0x7FFFFFFF;
-    int rank = 0;
-    for (int q0 = 0; q0 < n; q0 += 64) {
-      const uint32_t uq_l = q0 + lane < n ? F.cu[q0 + lane] : 0u;
-      const int iq_l = q0 + lane < n ? F.cid[q0 + lane] : 0x7FFFFFFF;
-      const int qn = min(64, n - q0);
-      for (int q = 0; q < qn; ++q) {
-        const uint32_t uq = (uint32_t)__builtin_amdgcn_readlane((int)uq_l, q);
-        const int iq = __builtin_amdgcn_readlane(iq_l, q);
-        rank += (uq > ut) || (uq == ut && iq < it);
-      }
-    }
-    if (t < n && rank == need_in - 1) { tu = ut; tb = it; }
-  }
-  const uint64_t fb = __ballot(tb >= 0);
-  if (!fb) return false;
-  const int src = __ffsll((unsigned long long)fb) - 1;
-  Tu_out = (uint32_t)__builtin_amdgcn_readlane((int)tu, src);
-  Tid_out = __builtin_amdgcn_readlane(tb, src);
-  return true;
+// Lanes of wave `wave` whose cluster s * 1024 + 64 wave + lane exists.
+__device__ __forceinline__ uint64_t slot_valid(int s, int wave, int c) {
+  const int r = c - s * kB1Threads - 64 * wave;
+  return r >= 64 ? ~0ull : r <= 0 ? 0ull : ((1ull << r) - 1ull);
 }
 
-// Rank structure of the kept bitmap: wave w owns words [64 w, 64 w + 64), one per lane;
-// S.woff[word] gets the kept count of the preceding words of the same wave slice and
-// F.wtot[1][w] the slice totals.  One barrier; call with the bitmap complete.
-template <int NWAVE>
-__device__ __forceinline__ void kept_index(SelShared& S, FastScratch& F, int nwords) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int w0 = wave * 64; w0 < kMaxWords; w0 += NWAVE * 64) {
-    const int w = w0 + lane;
-    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
-    const int incl = wave_incl_scan(pc);
-    S.woff[w] = incl - pc;
-    if (lane == 63) F.wtot[1][w0 >> 6] = incl;        // slices beyond NWAVE only when c > 64 NWAVE 32
-  }
-  __syncthreads();
-}
-
-// Cluster id of ascending rank q (wave-uniform q; all lanes get it).
-template <int NWAVE>
-__device__ __forceinline__ int kept_id(const SelShared& S, const FastScratch& F, int q) {
+// Cluster id of ascending rank q (wave-uniform) in the kept bitmap of nwords words; lane l
+// scans words [l WPL, l WPL + WPL).
+template <int WPL>
+__device__ __forceinline__ int kept_rank_id(const uint64_t* words, int nwords, int q) {
   const int lane = threadIdx.x & 63;
-  // slice holding rank q: slice totals live in F.wtot[1][0 .. kMaxWords / 64)
-  constexpr int NS = kMaxWords / 64;
-  const int tot = lane < NS ? F.wtot[1][lane] : 0;
-  const int incl = wave_incl_scan(tot);
-  const uint64_t in_slice = __ballot(lane < NS && incl > q);
-  const int sl = __ffsll((unsigned long long)in_slice) - 1;
-  const int sbase = __builtin_amdgcn_readlane(incl - tot, sl);
-  const int qq = q - sbase;
-  const int w = sl * 64 + lane;
-  const int off = S.woff[w];
-  const uint32_t bits = S.bitmap[w];
-  const uint64_t ok = __ballot(off <= qq && off + __popc(bits) > qq);
-  const int src = __ffsll((unsigned long long)ok) - 1;
-  int id = 0;
-  if (lane == src) {
-    uint32_t bb = bits;
-    for (int k = off; k < qq; ++k) bb &= bb - 1u;
-    id = (w << 5) + __ffs(bb) - 1;
+  uint64_t wv[WPL];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const int w = lane * WPL + i;
+    wv[i] = w < nwords ? words[w] : 0ull;
+    cnt += __popcll(wv[i]);
   }
-  return __builtin_amdgcn_readlane(id, src);
+  const int incl = wave_incl_scan(cnt);
+  const uint64_t hit = __ballot(incl > q);
+  const int L = __ffsll((unsigned long long)hit) - 1;
+  int id = 0;
+  if (lane == L) {
+    int r = q - (incl - cnt);
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      const int pc = __popcll(wv[i]);
+      if (r >= 0 && r < pc) {
+        uint64_t bits = wv[i];
+        for (int k = 0; k < r; ++k) bits &= bits - 1ull;
+        id = (lane * WPL + i) * 64 + __ffsll((unsigned long long)bits) - 1;
+      }
+      r -= pc;
+    }
+  }
+  return __builtin_amdgcn_readlane(id, L);
 }
 
-template <int RF, int CH, int NT, int KV>
-__global__ __launch_bounds__(NT) void k_b1_select_tiles(B1Params a) {
-  constexpr int NWAVE = NT / 64;
-  constexpr int MAXLIST = 256;      // probes per workgroup (p <= MAXLIST * gridDim.x)
+// Selection and stage 2 for one row in one kernel.  Every workgroup (1024 threads, one per
+// CU) reads the c keys and finds the same kept set: one float-linear histogram between the
+// key min and max locates the bin holding the p-th largest key, the keys of that bin are
+// ranked exactly (ties to the smaller cluster id), and the kept set is the keys above that
+// key plus the boundary ones it ranks in.  A boundary bin with more than 64 keys, or one
+// wave holding more than kS2Cap of them, sends the workgroup to the general selection
+// (select_regs).  Workgroup g then scores the kept clusters of ascending rank q = g (mod
+// gridDim.x) and writes the packed maximum of its tokens to part[g]; k_finalize_parts turns
+// the maxima into the token.  NS: key slots per thread, NR: tile rows per wave step.
+template <int RF, int CH, int NS, int NR>
+__global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
+  constexpr int NT = kB1Threads, NWAVE = NT / 64;
+  constexpr int KV = NS >= 4 ? NS / 4 : 1;             // uint4 per thread of the general selection
+  constexpr int WPL = NS >= 4 ? NS / 4 : 1;            // bitmap words per lane in kept_rank_id
+  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;  // h registers held across the selection
+  __shared__ __align__(16) S2Shared Q;
   __shared__ SelShared S;
-  __shared__ FastScratch F;
-  __shared__ int my_list[MAXLIST];
-  __shared__ uint64_t wmax[NWAVE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, me = blockIdx.x;
-  uint32_t u[KV][4];
-  load_keys<KV>(a.keys, a.c, u, S);        // also clears S.hist and S.bitmap
-  uint32_t vmax = 0u, vmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * (tid + j * NT) + e < a.c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
-  uint32_t Tu;
-  int Tid;
-  bool ok = select_fast<KV, NWAVE>(u, a.c, a.p, vmax, vmin, S, F, Tu, Tid);
-  if (!ok) {                                // wide boundary bin or equal keys: the general select
-    __syncthreads();
-    for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
-    __syncthreads();
-    select_regs<KV>(u, a.c, a.p, S, Tu, Tid);
-  }
-  // mark the kept set
-#pragma unroll
-  for (int j = 0; j < KV; ++j) {
-    const int id0 = 4 * (tid + j * NT);
-    uint32_t m = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int id = id0 + e;
-      m |= (id < a.c && (u[j][e] > Tu || (u[j][e] == Tu && id <= Tid))) ? (1u << e) : 0u;
-    }
-    if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
-  }
-  __syncthreads();
-  kept_index<NWAVE>(S, F, (a.c + 31) >> 5);
-  const int n_my = me < a.p ? (a.p - me + G - 1) / G : 0;
-  for (int i = wave; i < n_my; i += NWAVE) {
-    const int k = kept_id<NWAVE>(S, F, me + i * G);
-    if (lane == 0) my_list[i] = k;
-  }
-  if (me == 0 && a.probe_out)
-    for (int q = wave; q < a.p; q += NWAVE) {
-      const int k = kept_id<NWAVE>(S, F, q);
-      if (lane == 0) a.probe_out[q] = k;
-    }
-  __syncthreads();
-  // stage 2 on this workgroup's probes
+  const int c = a.c, p = a.p;
+  const int nwords = (c + 63) >> 6;
   HRegs<RF, CH> hr;
-  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  const int ngroups = (a.b + kRPI - 1) / kRPI;
+  if (kEarlyH) load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
+  // ---- keys; slots past c repeat cluster 0's key and are masked out of every count
+  const float key0 = a.keys[0];
+  float x[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int id = s * NT + tid;
+    if ((s + 1) * NT <= c) x[s] = a.keys[id];
+    else x[s] = id < c ? a.keys[id] : key0;
+  }
+  for (int i = tid; i < kSelBins; i += NT) Q.hist[i] = 0;
+  float mx = x[0], mn = x[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) { mx = fmaxf(mx, x[s]); mn = fminf(mn, x[s]); }
+  mx = wave_minmax_f32<true>(mx);
+  mn = wave_minmax_f32<false>(mn);
+  if (lane == 0) { Q.wmx[wave] = mx; Q.wmn[wave] = mn; }
+  __syncthreads();                                                          // 1
+  float hi = Q.wmx[0], lo = Q.wmn[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) { hi = fmaxf(hi, Q.wmx[w]); lo = fminf(lo, Q.wmn[w]); }
+  const float inv = (float)kSelBins / (hi - lo);
+  bool fast = hi > lo && inv > 0.f && inv < 3.0e38f;                        // block-uniform
+  const float off = -lo * inv;
+  auto bin_of = [&](float v) {
+    const int t = (int)fmaf(v, inv, off);
+    return min(max(t, 0), kSelBins - 1);
+  };
+  int bins[NS];
+  if (fast) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bins[s] = bin_of(x[s]);
+      atomicAdd(&Q.hist[bins[s]], 1);
+    }
+    if (tid == 0 && NS * NT > c) atomicSub(&Q.hist[bin_of(key0)], NS * NT - c);
+  }
+  __syncthreads();                                                          // 2
+  // ---- boundary bin: wave w sums bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
+  if (fast) {
+    const int top = kSelBins - 1 - 128 * wave - 2 * lane;
+    const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
+    const int incl = wave_incl_scan(hh.x + hh.y);
+    if (lane == 63) Q.wtot[wave] = incl;
+  }
+  __syncthreads();                                                          // 3
+  float T = 0.f;
+  int Tid = 0x7FFFFFFF;
+  bool uniq = false;
+  int b = 0, above = 0, inb = 0;
+  if (fast) {
+    int before = 0, bw = NWAVE - 1;
+    bool found = false;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const int t = Q.wtot[w];
+      if (!found && before + t >= p) { bw = w; found = true; }
+      if (!found) before += t;
+    }
+    // every wave rescans the boundary slice itself (no barrier)
+    const int top = kSelBins - 1 - 128 * bw - 2 * lane;
+    const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
+    const int local = hh.x + hh.y;
+    const int incl = wave_incl_scan(local) + before;
+    const uint64_t hit = __ballot(incl >= p);
+    const int L = __ffsll((unsigned long long)hit) - 1;
+    const int ex = incl - local;
+    const bool upper = ex + hh.y >= p;
+    b = __builtin_amdgcn_readlane(upper ? top : top - 1, L);
+    above = __builtin_amdgcn_readlane(upper ? ex : ex + hh.y, L);
+    inb = __builtin_amdgcn_readlane(upper ? hh.y : hh.x, L);
+    fast = found && b > 0 && inb <= 64;
+  }
+  // ---- gather the boundary bin's keys: per-wave slots, no atomics
+  if (fast) {
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      uint64_t m = __ballot(bins[s] == b);
+      if ((s + 1) * NT > c) m &= slot_valid(s, wave, c);
+      if (m) {
+        const int pos = cnt + lane_prefix(m);
+        if (((m >> lane) & 1ull) && pos < kS2Cap) { Q.cx[wave][pos] = x[s]; Q.cid[wave][pos] = s * NT + tid; }
+        cnt += __popcll(m);
+      }
+    }
+    if (lane == 0) Q.ccnt[wave] = cnt;
+  }
+  __syncthreads();                                                          // 4
+  if (fast) {
+    // lane t takes candidate t; every wave ranks them all by (key desc, id asc)
+    int pref[NWAVE + 1];
+    pref[0] = 0;
+    bool over = false;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      const int n_w = Q.ccnt[w];
+      over |= n_w > kS2Cap;
+      pref[w + 1] = pref[w] + n_w;
+    }
+    const int n = pref[NWAVE];
+    fast = !over && n == inb;
+    if (fast) {
+      int wt = 0;
+#pragma unroll
+      for (int w = 1; w < NWAVE; ++w) wt += pref[w] <= lane ? 1 : 0;
+      const bool act = lane < n;
+      const float xt = act ? Q.cx[wt][lane - pref[wt]] : 0.f;
+      const int it = act ? Q.cid[wt][lane - pref[wt]] : 0x7FFFFFFF;
+      int rank = 0;
+      for (int q = 0; q < n; ++q) {
+        const float xq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), q));
+        const int iq = __builtin_amdgcn_readlane(it, q);
+        rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
+      }
+      const uint64_t sel = __ballot(act && rank == p - above - 1);
+      const int src = __ffsll((unsigned long long)sel) - 1;
+      T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), src));
+      Tid = __builtin_amdgcn_readlane(it, src);
+      uniq = __popcll(__ballot(act && xt == T)) == 1;
+    }
+  }
+  if (!fast) {                                  // block-uniform: the general selection
+    uint32_t u[KV][4];
+    uint32_t Tu;
+    load_keys<KV>(a.keys, c, u, S);
+    select_regs<KV>(u, c, p, S, Tu, Tid);
+    T = ord_to_float(Tu);
+    uniq = false;
+  }
+  // ---- kept set: keys above T, and T's ties up to Tid
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    uint64_t m = __ballot(x[s] > T);
+    if (!uniq) m |= __ballot(x[s] == T && s * NT + tid <= Tid);
+    else if ((Tid >> 6) == s * NWAVE + wave) m |= 1ull << (Tid & 63);
+    if ((s + 1) * NT > c) m &= slot_valid(s, wave, c);
+    if (lane == 0 && s * NWAVE + wave < kS2MaxWords) Q.words[s * NWAVE + wave] = m;
+  }
+  __syncthreads();                                                          // 5
+  if (me == 0 && a.probe_out) {                 // all kept ids, ascending (workgroup 0)
+    int tot;
+    const int pc = tid < nwords ? __popcll(Q.words[tid]) : 0;
+    const int ex = block_scan(pc, Q.wtot, tot);
+    if (tid < nwords) Q.pref[tid] = ex;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int w = s * NWAVE + wave;
+      if (w < nwords) {
+        const uint64_t m = Q.words[w];
+        if ((m >> lane) & 1ull) a.probe_out[Q.pref[w] + lane_prefix(m)] = s * NT + tid;
+      }
+    }
+  }
+  // ---- stage 2 on this workgroup's probes
+  if (!kEarlyH) load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
+  const int n_my = me < p ? (p - me + G - 1) / G : 0;
+  const int gpp = (a.b + NR - 1) / NR;
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
   uint64_t bc = 0;
-  for (int it = wave; it < n_my * ngroups; it += NWAVE) {
-    const int qi = it / ngroups, j0 = (it % ngroups) * kRPI;
-    const int k = my_list[qi];
-    const int q = qi * G + me;
-    int tj[kRPI];
-#pragma unroll
-    for (int i = 0; i < kRPI; ++i) tj[i] = (j0 + i < a.b) ? a.c2t[(size_t)k * a.b + j0 + i] : 0;
-    RowGroup<RF, CH> g;
-    rows_load<RF, CH>(g, a.tiles + (size_t)k * a.b * rb, rb, j0, a.b,
-                      RF == RF_INT4 ? a.scales + (size_t)k * a.b * spr : nullptr, spr, lane);
-    float z[kRPI];
+  for (int it = wave; it < n_my * gpp; it += NWAVE) {
+    const int qi = it / gpp, j0 = (it - qi * gpp) * NR;
+    const int q = me + qi * G;
+    const int k = kept_rank_id<WPL>(Q.words, nwords, q);
+    const size_t row0 = (size_t)k * a.b;
+    const int tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
+    RowGroup<RF, CH, NR> g;
+    rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr, spr,
+                      lane);
+    float z[NR];
     rows_dot<RF, CH>(g, hr, z);
 #pragma unroll
-    for (int i = 0; i < kRPI; ++i) {
+    for (int i = 0; i < NR; ++i) {
       const int j = j0 + i;
-      if (lane == i && j < a.b) {
-        const int t = tj[i];
+      if (j < a.b) {
+        const int t = __builtin_amdgcn_readlane(tl, i);
         const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
         const uint64_t cnd = pack_cand(key, (uint32_t)t);
         bc = cnd > bc ? cnd : bc;
-        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = z[i];
-        if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
+        if (lane == 0) {
+          if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = z[i];
+          if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
+        }
       }
     }
   }
-  bc = wave_max_u64(bc);
-  if (lane == 0) wmax[wave] = bc;
+  if (lane == 0) Q.wmax[wave] = bc;
   __syncthreads();
   if (tid == 0) {
-    uint64_t m = wmax[0];
-    for (int w = 1; w < NWAVE; ++w) m = wmax[w] > m ? wmax[w] : m;
-    if (m) atomicMax((unsigned long long*)a.best, (unsigned long long)m);   // k_finalize decodes it
+    uint64_t m = Q.wmax[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) m = Q.wmax[w] > m ? Q.wmax[w] : m;
+    a.part[me] = m;
+  }
+}
+
+// The token of the fused B = 1 path: the largest of the per-workgroup maxima part[0 .. n).
+__global__ __launch_bounds__(256) void k_finalize_parts(const uint64_t* part, int n, int32_t* token) {
+  __shared__ uint64_t wm[4];
+  const int tid = threadIdx.x;
+  uint64_t m = 0;
+  for (int i = tid; i < n; i += 256) m = part[i] > m ? part[i] : m;
+  m = wave_max_u64(m);
+  if ((tid & 63) == 0) wm[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t r = wm[0];
+    for (int w = 1; w < 4; ++w) r = wm[w] > r ? wm[w] : r;
+    token[0] = (int32_t)cand_id(r);
   }
 }
 
@@ -1229,6 +1240,8 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   }
   w.best = (uint64_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * sizeof(uint64_t));
+  w.part = (uint64_t*)(b ? b + off : nullptr);
+  off = up(off + (size_t)kB1Workgroups * sizeof(uint64_t));
   w.probes = (int32_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * p * sizeof(int32_t));
   w.bytes = off;
@@ -1273,20 +1286,24 @@ static void launch_b1_scores(const B1Params& a, int c, hipStream_t st) {
   hipLaunchKernelGGL((k_b1_scores<RF, CH>), dim3(wgs), dim3(kThreads), 0, st, a);
 }
 
+template <int RF, int CH, int S>
+static void launch_b1_stage2_s(const B1Params& a, int G, int nr, hipStream_t st) {
+  if (nr == 1) hipLaunchKernelGGL((k_b1_stage2<RF, CH, S, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
+  else         hipLaunchKernelGGL((k_b1_stage2<RF, CH, S, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
+}
+
 template <int RF, int CH>
-static void launch_b1_stage2(const B1Params& a, int c, int p, hipStream_t st) {
-  int G = p < kB1Workgroups ? p : kB1Workgroups;
-  if (G < (p + 255) / 256) G = (p + 255) / 256;
-  const int kv = (c + 4 * kB1Threads - 1) / (4 * kB1Threads);   // uint4 of keys per thread
-  if (kv <= 1)
-    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
-  else if (kv <= 2)
-    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
-  else if (kv <= 4)
-    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 4>), dim3(G), dim3(kB1Threads), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_b1_select_tiles<RF, CH, kB1Threads, 8>), dim3(G), dim3(kB1Threads), 0, st, a);
-  hipLaunchKernelGGL(k_finalize, dim3(1), dim3(64), 0, st, a.best, a.token, 1);
+static void launch_b1_stage2(const B1Params& a, int c, int p, int b, hipStream_t st) {
+  const int G = p < kB1Workgroups ? p : kB1Workgroups;
+  const int n_my = (p + G - 1) / G;
+  const int nr = n_my * b <= kB1Threads / 64 ? 1 : 2;     // one row per wave when that fills them
+  const int slots = (c + kB1Threads - 1) / kB1Threads;
+  if (slots <= 2)       launch_b1_stage2_s<RF, CH, 2>(a, G, nr, st);
+  else if (slots <= 4)  launch_b1_stage2_s<RF, CH, 4>(a, G, nr, st);
+  else if (slots <= 8)  launch_b1_stage2_s<RF, CH, 8>(a, G, nr, st);
+  else if (slots <= 16) launch_b1_stage2_s<RF, CH, 16>(a, G, nr, st);
+  else                  launch_b1_stage2_s<RF, CH, 32>(a, G, nr, st);
+  hipLaunchKernelGGL(k_finalize_parts, dim3(1), dim3(256), 0, st, (const uint64_t*)a.part, G, a.token);
 }
 
 static bool use_mfma(const HeadShape& s, int fmt) {
@@ -1320,7 +1337,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     B1Params a{};
     a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
     a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
-    a.keys = ws.keys; a.keys_out = keys_out; a.best = ws.best;
+    a.keys = ws.keys; a.keys_out = keys_out;
     const int ch = chunk_slots(s.c_fmt, s.d);
     if (s.c_fmt == RF_F32) {
       FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
@@ -1393,16 +1410,16 @@ hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int3
   B1Params a{};
   a.h = h; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
   a.sample = smp.sample; a.tau = smp.tau; a.rng = make_rng(smp.seed, smp.step);
-  a.keys = ws.keys; a.best = ws.best;
+  a.keys = ws.keys; a.part = ws.part;
   a.c2t = c2t; a.tiles = (const char*)tiles; a.scales = scales;
   a.probe_out = probe_out; a.logits_out = logits_out; a.tokens_out = tokens_out; a.token = token;
   const int ch = chunk_slots(s.e_fmt, s.d);
   if (s.e_fmt == RF_F32) {
-    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_F32, kCH>(a, s.c, p, st)));
+    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_F32, kCH>(a, s.c, p, s.b, st)));
   } else if (s.e_fmt == RF_BF16) {
-    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_BF16, kCH>(a, s.c, p, st)));
+    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_BF16, kCH>(a, s.c, p, s.b, st)));
   } else {
-    FH_DISPATCH_CH_INT4(ch, (launch_b1_stage2<RF_INT4, kCH>(a, s.c, p, st)));
+    FH_DISPATCH_CH_INT4(ch, (launch_b1_stage2<RF_INT4, kCH>(a, s.c, p, s.b, st)));
   }
   return hipGetLastError();
 }

@@ -1,0 +1,92 @@
+"""GPU parity on degenerate stage-1 keys, where the probe selection must fall back from its
+one-histogram fast path to the general selection: every key equal, a long run of equal
+keys across the p-th place, and p = c.
+
+The inputs are built so that every score is computed exactly on both sides (h is zero or a
+one-hot vector, so each dot product has at most one non-zero term).  Ties are then exact,
+the order (larger key first, smaller id on ties) decides them, and the GPU must reproduce
+the oracle bit for bit: kept clusters, probe logits and token (FlashHead paper, Section
+3.2: top-p clusters by centroid score, argmax over the gathered tokens).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from clustered_retrieval_lm_amd.head import DeviceHead, to_device
+from oracle import codecs, kmeans
+from oracle import head as ohead
+
+from . import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _storage(a: np.ndarray, dt: str) -> np.ndarray:
+    return codecs.round_to_bf16(a) if dt == "bf16" else a.astype(np.float32)
+
+
+def _check_exact(dev: DeviceHead, h: np.ndarray, C: np.ndarray, C2T: np.ndarray, tiles, dt: str, p: int):
+    out = dev.forward(to_device(h, dev.device), p)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    ref = ohead.forward(h, dt, C, dt, C2T, tiles, p)
+    assert np.array_equal(got["probe_ids"][0], ref.probe_ids[0])
+    assert np.array_equal(got["probe_tokens"][0], ref.tokens[0])
+    assert np.array_equal(got["probe_logits"][0].astype(np.float64), ref.z[0])
+    assert got["token"][0] == ref.token[0]
+    return got, ref
+
+
+@pytest.mark.parametrize("c,p,dt", [(1003, 37, "bf16"), (16384, 512, "bf16"), (300, 20, "f32")])
+def test_all_keys_equal(gpu, c, p, dt):
+    d, b = 64, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=c + p, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    C = _storage(np.random.default_rng(c).standard_normal((c, d)), dt)
+    h = np.zeros((1, d), dtype=np.float32 if dt == "f32" else np.uint16)
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
+    assert np.array_equal(got["probe_ids"][0], np.arange(p))          # every score is 0
+    assert got["token"][0] == C2T[:p].min()                            # every logit is 0
+
+
+@pytest.mark.parametrize("c,p,run", [(1003, 250, 100), (8016, 256, 300), (16384, 512, 700)])
+def test_equal_run_across_the_boundary(gpu, c, p, run):
+    d, b, dt = 128, 16, "bf16"
+    hd = workloads.make_small(d, b * c, c, 1, seed=7 * c + p, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    Cf = np.zeros((c, d))
+    Cf[:, 0] = np.arange(c) // run                  # runs of `run` equal integer scores
+    C = _storage(Cf, dt)
+    hf = np.zeros((1, d))
+    hf[0, 0] = 1.0
+    h = _storage(hf, dt)
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
+    # the kept set: the top runs whole, then the smallest ids of the run holding the p-th key
+    order = np.lexsort((np.arange(c), -(np.arange(c) // run)))
+    assert np.array_equal(got["probe_ids"][0], np.sort(order[:p]))
+
+
+@pytest.mark.parametrize("c,dt", [(300, "bf16"), (1003, "f32")])
+def test_p_equals_c(gpu, c, dt):
+    d, b = 136, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=c, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    Ev = ohead.decode(hd.E, dt)
+    C = kmeans.centroids_from_c2t(Ev, C2T, dt)
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    out = dev.forward(to_device(hd.h, gpu), c)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["probe_ids"].cpu().numpy()[0], np.arange(c))
+    # p = c probes every token: the token is the dense head's
+    dense = ohead.dense_forward(hd.h, dt, hd.E, dt)
+    rep = H.Report()
+    ref = ohead.forward(hd.h, dt, C, dt, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), c)
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    H.compare_row(ref, 0, got["probe_ids"][0], got["probe_logits"][0], got["probe_tokens"][0], got["token"][0], c,
+                  H.L_stage1(1, dt, dt, d), H.L_gemv(dt, d), False, 1.0, 0, 0, dt == "f32", rep)
+    assert ref.token[0] == dense.token[0]
