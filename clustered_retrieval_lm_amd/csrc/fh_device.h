@@ -216,6 +216,71 @@ __device__ __forceinline__ void load_h(HRegs<RF, CH>& hr, const void* h, int h_b
   }
 }
 
+// h as loaded, before the conversion to fp32: the 16-byte words of each chunk slot (fp32
+// storage fills all W of them, bf16 storage the first half).  Lets a kernel issue the loads
+// of h early and convert after other loads are in flight.
+template <int RF, int CH>
+struct HRaw {
+  static constexpr int W = Fmt<RF>::EPC / 4;
+  uint4 r[CH][W];
+};
+
+template <int RF, int CH>
+__device__ __forceinline__ void load_h_raw(HRaw<RF, CH>& raw, const void* h, int h_bf16, int d, int lane) {
+  constexpr int EPC = Fmt<RF>::EPC, W = HRaw<RF, CH>::W;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int e0 = (lane + kWave * i) * EPC;
+    const bool ok = e0 < d;
+#pragma unroll
+    for (int v = 0; v < W; ++v) raw.r[i][v] = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) {
+      if (h_bf16) {
+        const uint16_t* src = (const uint16_t*)h + e0;
+        if (EPC >= 8) {
+#pragma unroll
+          for (int v = 0; v < EPC / 8; ++v) raw.r[i][v] = reinterpret_cast<const uint4*>(src)[v];
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(src);
+          raw.r[i][0] = make_uint4(w.x, w.y, 0u, 0u);
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>((const float*)h + e0);
+#pragma unroll
+        for (int v = 0; v < W; ++v) raw.r[i][v] = src[v];
+      }
+    }
+  }
+}
+
+template <int RF, int CH>
+__device__ __forceinline__ void unpack_h(HRegs<RF, CH>& hr, const HRaw<RF, CH>& raw, int h_bf16) {
+  constexpr int EPC = Fmt<RF>::EPC, W = HRaw<RF, CH>::W;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    if (h_bf16) {
+      constexpr int NV = EPC >= 8 ? EPC / 8 : 1, NJ = EPC >= 8 ? 4 : 2;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t ws[4] = {raw.r[i][v].x, raw.r[i][v].y, raw.r[i][v].z, raw.r[i][v].w};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          hr.v[i][8 * v + 2 * j] = bf16_lo(ws[j]);
+          hr.v[i][8 * v + 2 * j + 1] = bf16_hi(ws[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        hr.v[i][4 * v + 0] = __uint_as_float(raw.r[i][v].x);
+        hr.v[i][4 * v + 1] = __uint_as_float(raw.r[i][v].y);
+        hr.v[i][4 * v + 2] = __uint_as_float(raw.r[i][v].z);
+        hr.v[i][4 * v + 3] = __uint_as_float(raw.r[i][v].w);
+      }
+    }
+  }
+}
+
 // Partial dot of one 16-byte chunk with h (scale applies to int4 only).
 template <int RF>
 __device__ __forceinline__ float chunk_dot(const uint4 w, const float* hv, float acc, float scale);

@@ -567,6 +567,7 @@ struct B1Params {
   const void* h;
   const char* C;
   int h_bf16, c, d, b, p;
+  int cpad;             // keys padded with NaN up to this count
   int sample;
   float tau;
   Rng rng;
@@ -584,6 +585,8 @@ struct B1Params {
 
 template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
+  for (int i = a.c + blockIdx.x * kThreads + threadIdx.x; i < a.cpad; i += gridDim.x * kThreads)
+    a.keys[i] = __uint_as_float(0x7FC00000u);      // quiet NaN padding for k_b1_stage2
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
@@ -614,38 +617,49 @@ __device__ __forceinline__ int lane_prefix(uint64_t bal) {   // set bits of bal 
 // Shared state of k_b1_stage2.  Keys live in registers: slot s of thread t holds the key of
 // cluster s * 1024 + t, so one wave ballot covers 64 consecutive clusters and the kept set
 // is written as 64-bit words without atomics.
+// Key slots per thread of k_b1_stage2: the power of two >= c / 1024 (at least 2).  At B = 1
+// the workspace keys are padded to kB1Threads * slots with quiet NaNs, which every min, max
+// and comparison of the selection ignores.
+__host__ __device__ __forceinline__ int b1_key_slots(int c) {
+  int s = 2;
+  while (s * kB1Threads < c) s *= 2;
+  return s;
+}
+
 constexpr int kS2Cap = 16;                 // boundary-bin keys one wave may contribute
 constexpr int kS2MaxWords = 32768 / 64;
+constexpr int kS2MaxMine = 128;            // probes of one workgroup: ceil(p / gridDim.x)
 
 struct S2Shared {
   int hist[kSelBins];
-  uint64_t words[kS2MaxWords];             // bit i of word w: cluster 64 w + i is kept
-  int pref[kS2MaxWords];                   // kept clusters before word w (probe id output)
+  uint64_t words[kS2MaxWords];             // kept bitmap, wave-major: bit l of words[w NS + s]
+                                           // is cluster s 1024 + 64 w + l
+  int pref[kS2MaxWords];                   // kept clusters before id-ordered word i (probe ids)
   float wmx[16], wmn[16];
   int wtot[16];
   int ccnt[16];
   float cx[16][kS2Cap];
   int cid[16][kS2Cap];
   uint64_t wmax[16];
+  int bnd[3];                              // boundary bin, keys above it, keys in it
+  float T;                                 // the p-th largest key ...
+  int Tid, uniq, ok;                       // ... its cluster, whether no other key equals it
+  int mine[kS2MaxMine];                    // clusters of this workgroup's probes
 };
 
-// Lanes of wave `wave` whose cluster s * 1024 + 64 wave + lane exists.
-__device__ __forceinline__ uint64_t slot_valid(int s, int wave, int c) {
-  const int r = c - s * kB1Threads - 64 * wave;
-  return r >= 64 ? ~0ull : r <= 0 ? 0ull : ((1ull << r) - 1ull);
-}
-
-// Cluster id of ascending rank q (wave-uniform) in the kept bitmap of nwords words; lane l
-// scans words [l WPL, l WPL + WPL).
-template <int WPL>
-__device__ __forceinline__ int kept_rank_id(const uint64_t* words, int nwords, int q) {
+// Cluster id of ascending rank q (wave-uniform) in the kept bitmap.  The bitmap is stored
+// wave-major: words[w NS + s] covers clusters s 1024 + 64 w + [0, 64).  Lane l scans the
+// id-ordered words [l WPL, l WPL + WPL).
+template <int NS>
+__device__ __forceinline__ int kept_rank_id(const uint64_t* words, int q) {
+  constexpr int NW = NS * 16, WPL = NW >= 64 ? NW / 64 : 1;
   const int lane = threadIdx.x & 63;
   uint64_t wv[WPL];
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < WPL; ++i) {
-    const int w = lane * WPL + i;
-    wv[i] = w < nwords ? words[w] : 0ull;
+    const int iw = lane * WPL + i;
+    wv[i] = iw < NW ? words[(iw & 15) * NS + (iw >> 4)] : 0ull;
     cnt += __popcll(wv[i]);
   }
   const int incl = wave_incl_scan(cnt);
@@ -674,32 +688,28 @@ __device__ __forceinline__ int kept_rank_id(const uint64_t* words, int nwords, i
 // ranked exactly (ties to the smaller cluster id), and the kept set is the keys above that
 // key plus the boundary ones it ranks in.  A boundary bin with more than 64 keys, or one
 // wave holding more than kS2Cap of them, sends the workgroup to the general selection
-// (select_regs).  Workgroup g then scores the kept clusters of ascending rank q = g (mod
-// gridDim.x) and writes the packed maximum of its tokens to part[g]; k_finalize_parts turns
-// the maxima into the token.  NS: key slots per thread, NR: tile rows per wave step.
+// (select_regs).  The per-key steps run on all waves; each sequential step runs once, on
+// one wave, between barriers.  Workgroup g then scores the kept clusters of ascending rank
+// q = g (mod gridDim.x) and writes the packed maximum of its tokens to part[g];
+// k_finalize_parts turns the maxima into the token.  NS: key slots per thread, NR: tile
+// rows per wave step.
 template <int RF, int CH, int NS, int NR>
 __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   constexpr int NT = kB1Threads, NWAVE = NT / 64;
   constexpr int KV = NS >= 4 ? NS / 4 : 1;             // uint4 per thread of the general selection
-  constexpr int WPL = NS >= 4 ? NS / 4 : 1;            // bitmap words per lane in kept_rank_id
-  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;  // h registers held across the selection
+  constexpr int NWID = NS * 16;                        // 64-bit kept words, padding included
+  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;    // h loads issued before the selection
   __shared__ __align__(16) S2Shared Q;
   __shared__ SelShared S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, me = blockIdx.x;
   const int c = a.c, p = a.p;
-  const int nwords = (c + 63) >> 6;
-  HRegs<RF, CH> hr;
-  if (kEarlyH) load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  // ---- keys; slots past c repeat cluster 0's key and are masked out of every count
-  const float key0 = a.keys[0];
+  HRaw<RF, kEarlyH ? CH : 1> hraw;
+  if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
+  // ---- keys; the slots past c hold NaN: ignored by min / max, never greater or equal
   float x[NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int id = s * NT + tid;
-    if ((s + 1) * NT <= c) x[s] = a.keys[id];
-    else x[s] = id < c ? a.keys[id] : key0;
-  }
+  for (int s = 0; s < NS; ++s) x[s] = a.keys[s * NT + tid];
   for (int i = tid; i < kSelBins; i += NT) Q.hist[i] = 0;
   float mx = x[0], mn = x[0];
 #pragma unroll
@@ -714,62 +724,63 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   const float inv = (float)kSelBins / (hi - lo);
   bool fast = hi > lo && inv > 0.f && inv < 3.0e38f;                        // block-uniform
   const float off = -lo * inv;
-  auto bin_of = [&](float v) {
-    const int t = (int)fmaf(v, inv, off);
-    return min(max(t, 0), kSelBins - 1);
-  };
   int bins[NS];
   if (fast) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      bins[s] = bin_of(x[s]);
+    for (int s = 0; s < NS; ++s) {                 // NaN padding lands in bin 0
+      bins[s] = (int)fminf(fmaxf(fmaf(x[s], inv, off), 0.f), (float)(kSelBins - 1));
       atomicAdd(&Q.hist[bins[s]], 1);
     }
-    if (tid == 0 && NS * NT > c) atomicSub(&Q.hist[bin_of(key0)], NS * NT - c);
+    if (tid == 0 && NS * NT > c) atomicSub(&Q.hist[0], NS * NT - c);
   }
   __syncthreads();                                                          // 2
-  // ---- boundary bin: wave w sums bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
+  // ---- boundary bin: wave w scans bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
+  const int top = kSelBins - 1 - 128 * wave - 2 * lane;
+  int h_lo = 0, h_hi = 0, incl = 0;
   if (fast) {
-    const int top = kSelBins - 1 - 128 * wave - 2 * lane;
     const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
-    const int incl = wave_incl_scan(hh.x + hh.y);
+    h_lo = hh.x;
+    h_hi = hh.y;
+    incl = wave_incl_scan(h_lo + h_hi);
     if (lane == 63) Q.wtot[wave] = incl;
   }
   __syncthreads();                                                          // 3
-  float T = 0.f;
-  int Tid = 0x7FFFFFFF;
-  bool uniq = false;
-  int b = 0, above = 0, inb = 0;
   if (fast) {
-    int before = 0, bw = NWAVE - 1;
-    bool found = false;
+    int before = 0, bw = -1;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) {
       const int t = Q.wtot[w];
-      if (!found && before + t >= p) { bw = w; found = true; }
-      if (!found) before += t;
+      if (bw < 0) {
+        if (before + t >= p) bw = w;
+        else before += t;
+      }
     }
-    // every wave rescans the boundary slice itself (no barrier)
-    const int top = kSelBins - 1 - 128 * bw - 2 * lane;
-    const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
-    const int local = hh.x + hh.y;
-    const int incl = wave_incl_scan(local) + before;
-    const uint64_t hit = __ballot(incl >= p);
-    const int L = __ffsll((unsigned long long)hit) - 1;
-    const int ex = incl - local;
-    const bool upper = ex + hh.y >= p;
-    b = __builtin_amdgcn_readlane(upper ? top : top - 1, L);
-    above = __builtin_amdgcn_readlane(upper ? ex : ex + hh.y, L);
-    inb = __builtin_amdgcn_readlane(upper ? hh.y : hh.x, L);
-    fast = found && b > 0 && inb <= 64;
+    if (wave == bw) {                       // the slice holding the p-th key resolves it
+      const int cum = incl + before;
+      const int L = __ffsll((unsigned long long)__ballot(cum >= p)) - 1;
+      const int ex = cum - h_lo - h_hi;
+      if (lane == L) {
+        const bool upper = ex + h_hi >= p;
+        Q.bnd[0] = upper ? top : top - 1;
+        Q.bnd[1] = upper ? ex : ex + h_hi;
+        Q.bnd[2] = upper ? h_hi : h_lo;
+      }
+    }
+  }
+  __syncthreads();                                                          // 4
+  int b = 0, above = 0, inb = 0;
+  if (fast) {
+    b = Q.bnd[0];
+    above = Q.bnd[1];
+    inb = Q.bnd[2];
+    fast = b > 0 && inb <= 64;
   }
   // ---- gather the boundary bin's keys: per-wave slots, no atomics
   if (fast) {
     int cnt = 0;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      uint64_t m = __ballot(bins[s] == b);
-      if ((s + 1) * NT > c) m &= slot_valid(s, wave, c);
+      const uint64_t m = __ballot(bins[s] == b);
       if (m) {
         const int pos = cnt + lane_prefix(m);
         if (((m >> lane) & 1ull) && pos < kS2Cap) { Q.cx[wave][pos] = x[s]; Q.cid[wave][pos] = s * NT + tid; }
@@ -778,9 +789,8 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     }
     if (lane == 0) Q.ccnt[wave] = cnt;
   }
-  __syncthreads();                                                          // 4
-  if (fast) {
-    // lane t takes candidate t; every wave ranks them all by (key desc, id asc)
+  __syncthreads();                                                          // 5
+  if (fast && wave == 0) {                  // wave 0 ranks them by (key desc, id asc)
     int pref[NWAVE + 1];
     pref[0] = 0;
     bool over = false;
@@ -791,8 +801,8 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
       pref[w + 1] = pref[w] + n_w;
     }
     const int n = pref[NWAVE];
-    fast = !over && n == inb;
-    if (fast) {
+    const bool ok = !over && n == inb;
+    if (ok) {
       int wt = 0;
 #pragma unroll
       for (int w = 1; w < NWAVE; ++w) wt += pref[w] <= lane ? 1 : 0;
@@ -807,12 +817,23 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
       }
       const uint64_t sel = __ballot(act && rank == p - above - 1);
       const int src = __ffsll((unsigned long long)sel) - 1;
-      T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), src));
-      Tid = __builtin_amdgcn_readlane(it, src);
-      uniq = __popcll(__ballot(act && xt == T)) == 1;
+      const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), src));
+      const int nT = __popcll(__ballot(act && xt == T));
+      if (lane == src) { Q.T = T; Q.Tid = it; Q.uniq = nT == 1; }
     }
+    if (lane == 0) Q.ok = ok;
   }
-  if (!fast) {                                  // block-uniform: the general selection
+  __syncthreads();                                                          // 6
+  float T = 0.f;
+  int Tid = 0x7FFFFFFF;
+  bool uniq = false;
+  if (fast) {
+    fast = Q.ok;
+    T = Q.T;
+    Tid = Q.Tid;
+    uniq = Q.uniq;
+  }
+  if (!fast) {                              // block-uniform: the general selection
     uint32_t u[KV][4];
     uint32_t Tu;
     load_keys<KV>(a.keys, c, u, S);
@@ -820,34 +841,54 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     T = ord_to_float(Tu);
     uniq = false;
   }
-  // ---- kept set: keys above T, and T's ties up to Tid
+  // ---- kept set: keys above T, and T's ties up to Tid.  Lane s of each wave collects the
+  // wave's word of slot s; words are stored wave-major (words[wave NS + s]).
+  uint32_t wlo = 0u, whi = 0u;
+  if (uniq) {
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    uint64_t m = __ballot(x[s] > T);
-    if (!uniq) m |= __ballot(x[s] == T && s * NT + tid <= Tid);
-    else if ((Tid >> 6) == s * NWAVE + wave) m |= 1ull << (Tid & 63);
-    if ((s + 1) * NT > c) m &= slot_valid(s, wave, c);
-    if (lane == 0 && s * NWAVE + wave < kS2MaxWords) Q.words[s * NWAVE + wave] = m;
+    for (int s = 0; s < NS; ++s) {
+      const uint64_t m = __ballot(x[s] > T);
+      wlo = lane == s ? (uint32_t)m : wlo;
+      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+    }
+    if (wave == ((Tid >> 6) & (NWAVE - 1)) && lane == (Tid >> 10)) {
+      const int bit = Tid & 63;
+      if (bit < 32) wlo |= 1u << bit;
+      else whi |= 1u << (bit - 32);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint64_t m = __ballot(x[s] > T) | __ballot(x[s] == T && s * NT + tid <= Tid);
+      wlo = lane == s ? (uint32_t)m : wlo;
+      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+    }
   }
-  __syncthreads();                                                          // 5
-  if (me == 0 && a.probe_out) {                 // all kept ids, ascending (workgroup 0)
+  if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+  __syncthreads();                                                          // 7
+  if (me == 0 && a.probe_out) {             // all kept ids, ascending (workgroup 0)
     int tot;
-    const int pc = tid < nwords ? __popcll(Q.words[tid]) : 0;
+    const int pc = tid < NWID ? __popcll(Q.words[(tid & 15) * NS + (tid >> 4)]) : 0;
     const int ex = block_scan(pc, Q.wtot, tot);
-    if (tid < nwords) Q.pref[tid] = ex;
+    if (tid < NWID) Q.pref[tid] = ex;
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int w = s * NWAVE + wave;
-      if (w < nwords) {
-        const uint64_t m = Q.words[w];
-        if ((m >> lane) & 1ull) a.probe_out[Q.pref[w] + lane_prefix(m)] = s * NT + tid;
-      }
+      const uint64_t m = Q.words[wave * NS + s];
+      if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
     }
   }
-  // ---- stage 2 on this workgroup's probes
-  if (!kEarlyH) load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
+  // ---- this workgroup's probes: ranks me, me + G, ...; wave i finds the i-th
   const int n_my = me < p ? (p - me + G - 1) / G : 0;
+  for (int i = wave; i < n_my; i += NWAVE) {
+    const int k = kept_rank_id<NS>(Q.words, me + i * G);
+    if (lane == 0) Q.mine[i] = k;
+  }
+  __syncthreads();                                                          // 8
+  // ---- stage 2 on them
+  HRegs<RF, CH> hr;
+  if constexpr (kEarlyH) unpack_h<RF, CH>(hr, hraw, a.h_bf16);
+  else load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
   const int gpp = (a.b + NR - 1) / NR;
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
@@ -855,7 +896,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   for (int it = wave; it < n_my * gpp; it += NWAVE) {
     const int qi = it / gpp, j0 = (it - qi * gpp) * NR;
     const int q = me + qi * G;
-    const int k = kept_rank_id<WPL>(Q.words, nwords, q);
+    const int k = Q.mine[qi];
     const size_t row0 = (size_t)k * a.b;
     const int tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
     RowGroup<RF, CH, NR> g;
@@ -1232,7 +1273,7 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   size_t off = 0;
   char* b = (char*)base;
   w.keys = (float*)(b ? b + off : nullptr);
-  off = up(off + (size_t)B * c * sizeof(float));
+  off = up(off + (B == 1 ? (size_t)b1_key_slots(c) * kB1Threads : (size_t)B * c) * sizeof(float));
   w.mask = nullptr;
   if (B > 1) {
     w.mask = (uint64_t*)(b ? b + off : nullptr);
@@ -1337,7 +1378,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     B1Params a{};
     a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
     a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
-    a.keys = ws.keys; a.keys_out = keys_out;
+    a.keys = ws.keys; a.keys_out = keys_out; a.cpad = b1_key_slots(s.c) * kB1Threads;
     const int ch = chunk_slots(s.c_fmt, s.d);
     if (s.c_fmt == RF_F32) {
       FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
