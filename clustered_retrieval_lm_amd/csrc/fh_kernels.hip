@@ -626,30 +626,31 @@ __host__ __device__ __forceinline__ int b1_key_slots(int c) {
   return s;
 }
 
-constexpr int kS2Cap = 16;                 // boundary-bin keys one wave may contribute
 constexpr int kS2MaxWords = 32768 / 64;
-constexpr int kS2MaxMine = 128;            // probes of one workgroup: ceil(p / gridDim.x)
+constexpr int kS2MaxCand = 64;             // keys the boundary bin may hold on the fast path
 
 struct S2Shared {
   int hist[kSelBins];
-  uint64_t words[kS2MaxWords];             // kept bitmap, wave-major: bit l of words[w NS + s]
-                                           // is cluster s 1024 + 64 w + l
+  // Bitmaps over the clusters, wave-major: bit l of w[wave NS + s] is cluster s 1024 + 64 wave + l.
+  uint64_t words[kS2MaxWords];             // clusters certainly kept (or all kept, general path)
+  uint64_t fullw[kS2MaxWords];             // all kept clusters (probe outputs only)
   int pref[kS2MaxWords];                   // kept clusters before id-ordered word i (probe ids)
   float wmx[16], wmn[16];
   int wtot[16];
-  int ccnt[16];
-  float cx[16][kS2Cap];
-  int cid[16][kS2Cap];
-  uint64_t wmax[16];
   int bnd[3];                              // boundary bin, keys above it, keys in it
-  float T;                                 // the p-th largest key ...
-  int Tid, uniq, ok;                       // ... its cluster, whether no other key equals it
-  int mine[kS2MaxMine];                    // clusters of this workgroup's probes
+  int ncand;
+  float cx[kS2MaxCand];                    // the boundary bin's keys ...
+  int cid[kS2MaxCand];                     // ... and clusters
+  int bk[kS2MaxCand];                      // boundary clusters that are kept, ascending id
+  uint64_t wmax[16];
 };
 
-// Cluster id of ascending rank q (wave-uniform) in the kept bitmap.  The bitmap is stored
-// wave-major: words[w NS + s] covers clusters s 1024 + 64 w + [0, 64).  Lane l scans the
-// id-ordered words [l WPL, l WPL + WPL).
+// Position of id-ordered word iw in a wave-major bitmap with NS slots.
+template <int NS>
+__device__ __forceinline__ int wm_index(int iw) { return (iw & 15) * NS + (iw >> 4); }
+
+// Cluster id of ascending rank q (wave-uniform) among the set bits of a wave-major bitmap;
+// lane l scans the id-ordered words [l WPL, l WPL + WPL).
 template <int NS>
 __device__ __forceinline__ int kept_rank_id(const uint64_t* words, int q) {
   constexpr int NW = NS * 16, WPL = NW >= 64 ? NW / 64 : 1;
@@ -659,7 +660,7 @@ __device__ __forceinline__ int kept_rank_id(const uint64_t* words, int q) {
 #pragma unroll
   for (int i = 0; i < WPL; ++i) {
     const int iw = lane * WPL + i;
-    wv[i] = iw < NW ? words[(iw & 15) * NS + (iw >> 4)] : 0ull;
+    wv[i] = iw < NW ? words[wm_index<NS>(iw)] : 0ull;
     cnt += __popcll(wv[i]);
   }
   const int incl = wave_incl_scan(cnt);
@@ -682,35 +683,55 @@ __device__ __forceinline__ int kept_rank_id(const uint64_t* words, int q) {
   return __builtin_amdgcn_readlane(id, L);
 }
 
+// Set bits below cluster k (wave-uniform) in a wave-major bitmap: the ascending rank of k.
+template <int NS>
+__device__ __forceinline__ int kept_count_below(const uint64_t* words, int k) {
+  constexpr int NW = NS * 16, WPL = NW >= 64 ? NW / 64 : 1;
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < WPL; ++i) {
+    const int iw = lane * WPL + i;
+    if (iw < NW && iw <= (k >> 6)) {
+      const uint64_t w = words[wm_index<NS>(iw)];
+      cnt += __popcll(iw < (k >> 6) ? w : (w & ((1ull << (k & 63)) - 1ull)));
+    }
+  }
+  return __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+}
+
 // Selection and stage 2 for one row in one kernel.  Every workgroup (1024 threads, one per
-// CU) reads the c keys and finds the same kept set: one float-linear histogram between the
-// key min and max locates the bin holding the p-th largest key, the keys of that bin are
-// ranked exactly (ties to the smaller cluster id), and the kept set is the keys above that
-// key plus the boundary ones it ranks in.  A boundary bin with more than 64 keys, or one
-// wave holding more than kS2Cap of them, sends the workgroup to the general selection
-// (select_regs).  The per-key steps run on all waves; each sequential step runs once, on
-// one wave, between barriers.  Workgroup g then scores the kept clusters of ascending rank
-// q = g (mod gridDim.x) and writes the packed maximum of its tokens to part[g];
-// k_finalize_parts turns the maxima into the token.  NS: key slots per thread, NR: tile
-// rows per wave step.
+// CU) reads the c keys and finds the same kept set, so no workgroup waits for another:
+//  * one float-linear 2048-bin histogram between the key min and max locates the bin b
+//    holding the p-th largest key; every key in a bin above b is certainly kept;
+//  * the clusters are numbered 0 .. p-1 in this order: the certain ones by ascending id,
+//    then the kept keys of bin b by ascending id; workgroup g takes the numbers g, g + G, ..;
+//  * the certain clusters are resolved and their tile loads issued while wave 0 ranks the
+//    keys of bin b exactly (key desc, id asc) to pick the p - above of them that are kept.
+// A boundary bin with more than kS2MaxCand keys (or all keys equal) sends the workgroup to
+// the general selection (select_regs), after which every cluster is resolved from the full
+// kept bitmap.  Each workgroup writes the packed maximum of its tokens to part[g];
+// k_finalize_parts turns the maxima into the token.  Probe outputs are indexed by the
+// ascending rank of the cluster among all kept ones.  NS: key slots per thread, NR: tile rows
+// per wave step.
 template <int RF, int CH, int NS, int NR>
 __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   constexpr int NT = kB1Threads, NWAVE = NT / 64;
   constexpr int KV = NS >= 4 ? NS / 4 : 1;             // uint4 per thread of the general selection
-  constexpr int NWID = NS * 16;                        // 64-bit kept words, padding included
-  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;    // h loads issued before the selection
+  constexpr int NWID = NS * 16;                        // 64-bit bitmap words, padding included
+  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;    // h loads issued with the first tile rows
   __shared__ __align__(16) S2Shared Q;
   __shared__ SelShared S;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, me = blockIdx.x;
   const int c = a.c, p = a.p;
-  HRaw<RF, kEarlyH ? CH : 1> hraw;
-  if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
+  const bool want = a.probe_out || a.logits_out || a.tokens_out;
   // ---- keys; the slots past c hold NaN: ignored by min / max, never greater or equal
   float x[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) x[s] = a.keys[s * NT + tid];
   for (int i = tid; i < kSelBins; i += NT) Q.hist[i] = 0;
+  if (tid == 0) Q.ncand = 0;
   float mx = x[0], mn = x[0];
 #pragma unroll
   for (int s = 1; s < NS; ++s) { mx = fmaxf(mx, x[s]); mn = fminf(mn, x[s]); }
@@ -773,137 +794,142 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     b = Q.bnd[0];
     above = Q.bnd[1];
     inb = Q.bnd[2];
-    fast = b > 0 && inb <= 64;
+    fast = b > 0 && inb <= kS2MaxCand;
   }
-  // ---- gather the boundary bin's keys: per-wave slots, no atomics
+  // ---- the certain clusters (bins above b) as a bitmap; the keys of bin b compacted
   if (fast) {
-    int cnt = 0;
+    uint32_t wlo = 0u, whi = 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint64_t m = __ballot(bins[s] == b);
-      if (m) {
-        const int pos = cnt + lane_prefix(m);
-        if (((m >> lane) & 1ull) && pos < kS2Cap) { Q.cx[wave][pos] = x[s]; Q.cid[wave][pos] = s * NT + tid; }
-        cnt += __popcll(m);
+      const uint64_t m = __ballot(bins[s] > b);
+      wlo = lane == s ? (uint32_t)m : wlo;
+      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+      const uint64_t e = __ballot(bins[s] == b);
+      if (e) {
+        int base = 0;
+        if (lane == __ffsll((unsigned long long)e) - 1) base = atomicAdd(&Q.ncand, __popcll(e));
+        base = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(base, __ffsll((unsigned long long)e) - 1));
+        const int pos = base + lane_prefix(e);
+        if (bins[s] == b && pos < kS2MaxCand) { Q.cx[pos] = x[s]; Q.cid[pos] = s * NT + tid; }
       }
     }
-    if (lane == 0) Q.ccnt[wave] = cnt;
+    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
   }
   __syncthreads();                                                          // 5
-  if (fast && wave == 0) {                  // wave 0 ranks them by (key desc, id asc)
-    int pref[NWAVE + 1];
-    pref[0] = 0;
-    bool over = false;
+  if (fast) fast = Q.ncand == inb;          // block-uniform
+  int n_def = above;                        // numbers below n_def index Q.words
+  if (!fast) {                              // the general selection, then the full kept bitmap
+    uint32_t u[KV][4];
+    uint32_t Tu;
+    int Tid;
+    load_keys<KV>(a.keys, c, u, S);
+    select_regs<KV>(u, c, p, S, Tu, Tid);
+    const float T = ord_to_float(Tu);
+    uint32_t wlo = 0u, whi = 0u;
 #pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const int n_w = Q.ccnt[w];
-      over |= n_w > kS2Cap;
-      pref[w + 1] = pref[w] + n_w;
+    for (int s = 0; s < NS; ++s) {
+      const float v = a.keys[s * NT + tid];
+      const uint64_t m = __ballot(v > T) | __ballot(v == T && s * NT + tid <= Tid);
+      wlo = lane == s ? (uint32_t)m : wlo;
+      whi = lane == s ? (uint32_t)(m >> 32) : whi;
     }
-    const int n = pref[NWAVE];
-    const bool ok = !over && n == inb;
-    if (ok) {
-      int wt = 0;
-#pragma unroll
-      for (int w = 1; w < NWAVE; ++w) wt += pref[w] <= lane ? 1 : 0;
+    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+    n_def = p;
+  }
+  const int n_my = me < p ? (p - me + G - 1) / G : 0;
+  const int gpp = (a.b + NR - 1) / NR;
+  const int nit = n_my * gpp;
+  const int rb = row_bytes_of(RF, a.d);
+  const int spr = a.d >> 7;
+  // this wave's first tile rows, when certain: resolved and loaded while wave 0 ranks
+  RowGroup<RF, CH, NR> g0;
+  int tl0 = 0, k0 = -1;
+  HRaw<RF, CH> hraw;
+  if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
+  if (fast) {
+    if (wave == 0) {                        // rank the boundary keys; keep the first p - above
+      const int n = inb;
+      const int need = p - above;
       const bool act = lane < n;
-      const float xt = act ? Q.cx[wt][lane - pref[wt]] : 0.f;
-      const int it = act ? Q.cid[wt][lane - pref[wt]] : 0x7FFFFFFF;
+      const float xt = act ? Q.cx[lane] : 0.f;
+      const int it = act ? Q.cid[lane] : 0x7FFFFFFF;
       int rank = 0;
       for (int q = 0; q < n; ++q) {
         const float xq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), q));
         const int iq = __builtin_amdgcn_readlane(it, q);
         rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
       }
-      const uint64_t sel = __ballot(act && rank == p - above - 1);
-      const int src = __ffsll((unsigned long long)sel) - 1;
-      const float T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), src));
-      const int nT = __popcll(__ballot(act && xt == T));
-      if (lane == src) { Q.T = T; Q.Tid = it; Q.uniq = nT == 1; }
+      const bool kept = act && rank < need;
+      int pos = 0;
+      for (int q = 0; q < n; ++q) {
+        const int rq = __builtin_amdgcn_readlane(rank, q);
+        const int iq = __builtin_amdgcn_readlane(it, q);
+        pos += (rq < need && iq < it) ? 1 : 0;
+      }
+      if (kept) Q.bk[pos] = it;
     }
-    if (lane == 0) Q.ok = ok;
+    if (wave < nit) {
+      const int qi = wave / gpp, j0 = (wave - qi * gpp) * NR;
+      const int q = me + qi * G;
+      if (q < above) {
+        k0 = kept_rank_id<NS>(Q.words, q);
+        const size_t row0 = (size_t)k0 * a.b;
+        tl0 = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
+        rows_load<RF, CH>(g0, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
+                          spr, lane);
+      }
+    }
   }
   __syncthreads();                                                          // 6
-  float T = 0.f;
-  int Tid = 0x7FFFFFFF;
-  bool uniq = false;
-  if (fast) {
-    fast = Q.ok;
-    T = Q.T;
-    Tid = Q.Tid;
-    uniq = Q.uniq;
-  }
-  if (!fast) {                              // block-uniform: the general selection
-    uint32_t u[KV][4];
-    uint32_t Tu;
-    load_keys<KV>(a.keys, c, u, S);
-    select_regs<KV>(u, c, p, S, Tu, Tid);
-    T = ord_to_float(Tu);
-    uniq = false;
-  }
-  // ---- kept set: keys above T, and T's ties up to Tid.  Lane s of each wave collects the
-  // wave's word of slot s; words are stored wave-major (words[wave NS + s]).
-  uint32_t wlo = 0u, whi = 0u;
-  if (uniq) {
+  // ---- probe outputs: the full kept bitmap gives every cluster its ascending rank
+  const uint64_t* fw = fast ? Q.fullw : Q.words;
+  if (want) {
+    if (fast) {
+      for (int i = tid; i < NWID; i += NT) Q.fullw[i] = Q.words[i];
+      __syncthreads();
+      if (tid < p - above) {
+        const int k = Q.bk[tid];
+        atomicOr((unsigned long long*)&Q.fullw[(((k >> 6) & 15) * NS) + (k >> 10)], 1ull << (k & 63));
+      }
+      __syncthreads();
+    }
+    if (me == 0 && a.probe_out) {
+      int tot;
+      const int pc = tid < NWID ? __popcll(fw[wm_index<NS>(tid)]) : 0;
+      const int ex = block_scan(pc, Q.wtot, tot);
+      if (tid < NWID) Q.pref[tid] = ex;
+      __syncthreads();
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint64_t m = __ballot(x[s] > T);
-      wlo = lane == s ? (uint32_t)m : wlo;
-      whi = lane == s ? (uint32_t)(m >> 32) : whi;
-    }
-    if (wave == ((Tid >> 6) & (NWAVE - 1)) && lane == (Tid >> 10)) {
-      const int bit = Tid & 63;
-      if (bit < 32) wlo |= 1u << bit;
-      else whi |= 1u << (bit - 32);
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint64_t m = __ballot(x[s] > T) | __ballot(x[s] == T && s * NT + tid <= Tid);
-      wlo = lane == s ? (uint32_t)m : wlo;
-      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+      for (int s = 0; s < NS; ++s) {
+        const uint64_t m = fw[wave * NS + s];
+        if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
+      }
     }
   }
-  if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-  __syncthreads();                                                          // 7
-  if (me == 0 && a.probe_out) {             // all kept ids, ascending (workgroup 0)
-    int tot;
-    const int pc = tid < NWID ? __popcll(Q.words[(tid & 15) * NS + (tid >> 4)]) : 0;
-    const int ex = block_scan(pc, Q.wtot, tot);
-    if (tid < NWID) Q.pref[tid] = ex;
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint64_t m = Q.words[wave * NS + s];
-      if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
-    }
-  }
-  // ---- this workgroup's probes: ranks me, me + G, ...; wave i finds the i-th
-  const int n_my = me < p ? (p - me + G - 1) / G : 0;
-  for (int i = wave; i < n_my; i += NWAVE) {
-    const int k = kept_rank_id<NS>(Q.words, me + i * G);
-    if (lane == 0) Q.mine[i] = k;
-  }
-  __syncthreads();                                                          // 8
-  // ---- stage 2 on them
+  // ---- stage 2 on this workgroup's clusters
   HRegs<RF, CH> hr;
   if constexpr (kEarlyH) unpack_h<RF, CH>(hr, hraw, a.h_bf16);
   else load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  const int gpp = (a.b + NR - 1) / NR;
-  const int rb = row_bytes_of(RF, a.d);
-  const int spr = a.d >> 7;
   uint64_t bc = 0;
-  for (int it = wave; it < n_my * gpp; it += NWAVE) {
+  for (int it = wave; it < nit; it += NWAVE) {
     const int qi = it / gpp, j0 = (it - qi * gpp) * NR;
     const int q = me + qi * G;
-    const int k = Q.mine[qi];
-    const size_t row0 = (size_t)k * a.b;
-    const int tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
+    int k, tl;
     RowGroup<RF, CH, NR> g;
-    rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr, spr,
-                      lane);
+    if (it == wave && k0 >= 0) {
+      k = k0;
+      tl = tl0;
+      g = g0;
+    } else {
+      k = q < n_def ? kept_rank_id<NS>(Q.words, q) : Q.bk[q - n_def];
+      const size_t row0 = (size_t)k * a.b;
+      tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
+      rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
+                        spr, lane);
+    }
     float z[NR];
     rows_dot<RF, CH>(g, hr, z);
+    const int qo = want ? kept_count_below<NS>(fw, k) : 0;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int j = j0 + i;
@@ -912,9 +938,9 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
         const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
         const uint64_t cnd = pack_cand(key, (uint32_t)t);
         bc = cnd > bc ? cnd : bc;
-        if (lane == 0) {
-          if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = z[i];
-          if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
+        if (want && lane == 0) {
+          if (a.logits_out) a.logits_out[(size_t)qo * a.b + j] = z[i];
+          if (a.tokens_out) a.tokens_out[(size_t)qo * a.b + j] = t;
         }
       }
     }
