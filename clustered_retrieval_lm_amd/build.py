@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libflashhead.so")
-SOURCES = ["fh_kernels.hip", "fh_api.hip"]
+SOURCES = ["fh_kernels.hip", "fh_cluster.hip", "fh_api.hip"]
 HEADERS = ["fh_device.h", "fh_internal.h"]
 ARCH = os.environ.get("FLASHHEAD_ARCH", "gfx950")
 

@@ -169,6 +169,43 @@ fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void
   return FH_OK;
 }
 
+static fh_status check_clusters_args(const fh_desc* desc, int32_t src_dtype) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (src_dtype != FH_F32 && src_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "src_dtype must be F32 or BF16");
+  if (desc->c > kMaxC) return fail(FH_ERR_UNSUPPORTED, "c=%lld exceeds %lld", (long long)desc->c, (long long)kMaxC);
+  if (desc->V / desc->c > kMaxTile)
+    return fail(FH_ERR_UNSUPPORTED, "cluster size b=%lld exceeds %lld", (long long)(desc->V / desc->c),
+                (long long)kMaxTile);
+  return FH_OK;
+}
+
+fh_status flashhead_build_clusters_workspace_bytes(const fh_desc* desc, int32_t src_dtype, size_t* bytes) {
+  fh_status st = check_clusters_args(desc, src_dtype);
+  if (st != FH_OK) return st;
+  if (!bytes) return fail(FH_ERR_ARG, "bytes is NULL");
+  *bytes = fh::build_clusters_workspace_bytes((int)desc->V, (int)desc->d, (int)desc->c);
+  return FH_OK;
+}
+
+fh_status flashhead_build_clusters(const fh_desc* desc, int32_t src_dtype, const void* E, int32_t iters,
+                                   uint64_t seed, int32_t unit, void* centroids, int32_t* cluster_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  fh_status st = check_clusters_args(desc, src_dtype);
+  if (st != FH_OK) return st;
+  if (iters < 1 || iters > 100000) return fail(FH_ERR_ARG, "iters=%d must be in [1, 100000]", (int)iters);
+  if (unit != 0 && unit != 1) return fail(FH_ERR_ARG, "unit must be 0 or 1");
+  if (!E || !centroids || !cluster_tokens) return fail(FH_ERR_ARG, "E, centroids and cluster_tokens must be non-NULL");
+  const size_t need = fh::build_clusters_workspace_bytes((int)desc->V, (int)desc->d, (int)desc->c);
+  if (!workspace || workspace_bytes < need)
+    return fail(FH_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+  hipError_t e = fh::launch_build_clusters((int)desc->V, (int)desc->d, (int)desc->c, src_dtype == FH_BF16, E, iters,
+                                           seed, unit, desc->c_dtype == FH_BF16, centroids, cluster_tokens, workspace,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "build_clusters");
+  return FH_OK;
+}
+
 fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const void* centroids, int32_t mode,
                                     float temperature, uint64_t seed, uint64_t step, void* workspace,
                                     size_t workspace_bytes, float* keys_out, void* stream) {

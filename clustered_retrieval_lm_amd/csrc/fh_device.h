@@ -43,12 +43,16 @@ __device__ __forceinline__ uint32_t cand_id(uint64_t c) { return 0xFFFFFFFFu - (
 
 // ---------------------------------------------------------------- Philox4x32-10
 // Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers: As Easy as 1, 2, 3" (SC'11).
-__device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
+__host__ __device__ __forceinline__ uint32_t mulhi32(uint32_t a, uint32_t b) {
+  return (uint32_t)(((uint64_t)a * b) >> 32);
+}
+
+__host__ __device__ __forceinline__ uint4 philox4x32_10(uint4 x, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
     if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-    const uint32_t a0 = 0xD2511F53u * x.x, h0 = __umulhi(0xD2511F53u, x.x);
-    const uint32_t a1 = 0xCD9E8D57u * x.z, h1 = __umulhi(0xCD9E8D57u, x.z);
+    const uint32_t a0 = 0xD2511F53u * x.x, h0 = mulhi32(0xD2511F53u, x.x);
+    const uint32_t a1 = 0xCD9E8D57u * x.z, h1 = mulhi32(0xCD9E8D57u, x.z);
     x = make_uint4(h1 ^ x.y ^ k0, a1, h0 ^ x.w ^ k1, a0);
   }
   return x;
@@ -63,7 +67,7 @@ __host__ __device__ inline Rng make_rng(uint64_t seed, uint64_t step) {
 }
 
 // The word for element n of (row, stream).
-__device__ __forceinline__ uint32_t rng_word(const Rng& g, uint32_t row, uint32_t stream, uint32_t n) {
+__host__ __device__ __forceinline__ uint32_t rng_word(const Rng& g, uint32_t row, uint32_t stream, uint32_t n) {
   uint4 ctr = make_uint4(n >> 2, row, g.step_lo, g.step_hi4 | stream);
   uint4 o = philox4x32_10(ctr, g.k0, g.k1);
   const uint32_t s = n & 3u;
@@ -71,7 +75,7 @@ __device__ __forceinline__ uint32_t rng_word(const Rng& g, uint32_t row, uint32_
 }
 
 // Odd multiples of 2^-24 in (0, 1): exact in fp32.
-__device__ __forceinline__ float word_to_uniform(uint32_t w) {
+__host__ __device__ __forceinline__ float word_to_uniform(uint32_t w) {
   return (float)(2u * (w >> 9) + 1u) * 0x1p-24f;
 }
 

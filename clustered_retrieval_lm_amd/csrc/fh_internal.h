@@ -58,6 +58,10 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
                         uint64_t* best, int32_t* token, float* logits, hipStream_t st);
 hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int unit, const void* E,
                             const int32_t* c2t, void* out, hipStream_t st);
+// Offline balanced spherical k-means (fh_cluster.hip); synchronises `st` once per round.
+size_t build_clusters_workspace_bytes(int V, int d, int c);
+hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* E, int iters, uint64_t seed, int unit,
+                                 int dst_bf16, void* centroids, int32_t* c2t, void* ws, hipStream_t st);
 hipError_t launch_pack(int V, int d, int c, int b, int src_bf16, int dst_fmt, const void* E,
                        const int32_t* c2t, void* tiles, uint16_t* scales, uint32_t* counts,
                        uint32_t* bad, hipStream_t st);

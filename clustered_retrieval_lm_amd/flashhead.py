@@ -65,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_workspace_bytes": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_pack": ([D, i32, vp, vp, vp, vp, vp], ctypes.c_int),
         "flashhead_centroids": ([D, i32, vp, vp, i32, vp, vp], ctypes.c_int),
+        "flashhead_build_clusters_workspace_bytes": ([D, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "flashhead_build_clusters": ([D, i32, vp, i32, u64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "flashhead_centroid_scores": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_select_probes": ([D, i64, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_probe_logits": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
@@ -159,6 +161,21 @@ def flashhead_centroids(desc: fh_desc, src_dtype, E, cluster_tokens, centroids, 
     src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
     _check(load_library().flashhead_centroids(ctypes.byref(desc), src, _ptr(E), _ptr(cluster_tokens), int(bool(unit)),
                                               _ptr(centroids), _stream(stream)))
+
+
+def flashhead_build_clusters_workspace_bytes(desc: fh_desc, src_dtype) -> int:
+    src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
+    n = ctypes.c_size_t(0)
+    _check(load_library().flashhead_build_clusters_workspace_bytes(ctypes.byref(desc), src, ctypes.byref(n)))
+    return n.value
+
+
+def flashhead_build_clusters(desc: fh_desc, src_dtype, E, iters, seed, unit, centroids, cluster_tokens, workspace,
+                             stream=None) -> None:
+    src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
+    _check(load_library().flashhead_build_clusters(
+        ctypes.byref(desc), src, _ptr(E), int(iters), int(seed), int(bool(unit)), _ptr(centroids),
+        _ptr(cluster_tokens), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def flashhead_centroid_scores(desc: fh_desc, h, centroids, mode, temperature, seed, step, workspace,

@@ -125,6 +125,35 @@ fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E,
                          void* stream);
 
 /*
+ * Offline balanced spherical k-means (Section 3.1, "Clustering the Embedding Matrix"): c
+ * clusters of exactly b = V / c tokens each.  Rows are normalised; the centres start from
+ * k-means++ in the spherical metric (weights 2 - 2 cos; draw m uses Philox4x32-10 keyed by
+ * `seed`, stream 2, row 0, step m, element 0, by inverse CDF over the weight prefix sums in
+ * ascending token id); each of `iters` rounds assigns every token its most similar centre,
+ * lets an over-full cluster keep its b most similar members (ties: smaller token id) and
+ * places the evicted tokens, in ascending id, on the most similar cluster with room (ties:
+ * smaller cluster id), then sets c_k = normalise(sum of the members' unit rows).  The page
+ * fixes neither the initialisation, the iteration count nor these orders; they are this
+ * library's readings.  All arithmetic is fp64 with fixed reduction orders and stable
+ * sorts, so the result does not depend on scheduling.
+ *   desc           V, d, c (b = V / c <= 256, c <= 32768); desc->c_dtype: stored centroids
+ *   src_dtype      dtype of E (F32 | BF16)
+ *   E              device, [V][d] token-major embeddings
+ *   iters          >= 1 rounds
+ *   unit           0: stored centroid = mean of the members' raw rows (as flashhead_centroids);
+ *                  1: the unit centroid c_k of the last round
+ *   centroids      device out, [c][d] in desc->c_dtype (rounded once, to nearest even)
+ *   cluster_tokens device out, int32 [c][b]: C2T, members in ascending token id
+ *   workspace      device, >= flashhead_build_clusters_workspace_bytes (about 8 V d bytes)
+ * Offline: launches thousands of kernels (two per k-means++ draw) and synchronises
+ * `stream` once per round.
+ */
+fh_status flashhead_build_clusters_workspace_bytes(const fh_desc* desc, int32_t src_dtype, size_t* bytes);
+fh_status flashhead_build_clusters(const fh_desc* desc, int32_t src_dtype, const void* E, int32_t iters,
+                                   uint64_t seed, int32_t unit, void* centroids, int32_t* cluster_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Offline centroids of a given clustering (Section 3.1, "Centroid matrix").
  *   E              device, [V][d] token-major embeddings of dtype src_dtype (F32 | BF16)
  *   cluster_tokens device, int32 [c][b]: C2T

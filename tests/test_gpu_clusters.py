@@ -1,0 +1,90 @@
+"""GPU balanced spherical k-means (flashhead_build_clusters) against the CPU oracle.
+
+Both sides follow the FlashHead paper, Section 3.1 (balanced spherical k-means), with the
+same readings (k-means++ draws from Philox stream 2, evicted tokens placed in ascending id,
+ties to the smaller id).  Both compute in fp64; their sums run in different orders, so a
+decision can only differ where two candidates are within rounding of each other -- none is
+expected on these inputs, and the tests ask for identical clusterings.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from clustered_retrieval_lm_amd import flashhead as fh
+from clustered_retrieval_lm_amd.head import to_device
+from oracle import codecs, kmeans
+from oracle import head as ohead
+
+from . import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_build(E, src, V, d, c, iters, seed, unit, dst, dev):
+    desc = fh.make_desc(1, d, V, c, src, dst, src)
+    ws = torch.empty(fh.flashhead_build_clusters_workspace_bytes(desc, src), dtype=torch.uint8, device=dev)
+    cent = torch.empty(c * d, dtype=torch.int16 if dst == "bf16" else torch.float32, device=dev)
+    c2t = torch.empty(V, dtype=torch.int32, device=dev)
+    fh.flashhead_build_clusters(desc, src, to_device(E, dev), iters, seed, unit, cent, c2t, ws)
+    torch.cuda.synchronize()
+    C = cent.cpu().numpy().reshape(c, d)
+    return (C.view(np.uint16) if dst == "bf16" else C), c2t.cpu().numpy().reshape(c, V // c)
+
+
+def _check_balanced(C2T, V, c):
+    assert C2T.shape == (c, V // c)
+    assert np.array_equal(np.sort(C2T.reshape(-1)), np.arange(V))        # a permutation: every token once
+    assert np.all(np.diff(C2T, axis=1) > 0)                               # members in ascending id
+
+
+def test_tiny_head_matches_the_stored_oracle_clustering(gpu):
+    wl, hd, C2T_ref, C_ref = H.load("tiny")
+    C, C2T = _gpu_build(hd.E, "f32", wl.V, wl.d, wl.c, wl.kmeans_iters, wl.data_seed, False, "f32", gpu)
+    _check_balanced(C2T, wl.V, wl.c)
+    assert np.array_equal(C2T, C2T_ref)
+    assert np.array_equal(C, C_ref)
+
+
+@pytest.mark.parametrize("unit", [False, True])
+def test_small_bf16_head_matches_the_oracle(gpu, unit):
+    d, c, b = 128, 300, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=11, sigma_c=1.0, sigma_n=0.5, dtype="bf16")
+    Ev = ohead.decode(hd.E, "bf16")
+    C_ref, C2T_ref = kmeans.build_clusters(Ev, c, iters=4, seed=5, unit=unit, out_dtype="bf16")
+    C, C2T = _gpu_build(hd.E, "bf16", b * c, d, c, 4, 5, unit, "bf16", gpu)
+    _check_balanced(C2T, b * c, c)
+    assert np.array_equal(C2T, C2T_ref)
+    if unit:     # both round the same unit vector; its fp64 sums differ only in order
+        diff = np.abs(C.astype(np.int32) - C_ref.astype(np.int32))
+        assert diff.max() <= 1
+    else:
+        assert np.array_equal(C, C_ref)
+
+
+def test_mid_size_invariants_and_determinism(gpu):
+    d, c, b = 256, 2048, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=3, sigma_c=0.02, sigma_n=0.01, dtype="bf16")
+    C1, T1 = _gpu_build(hd.E, "bf16", b * c, d, c, 3, 0, False, "bf16", gpu)
+    C2, T2 = _gpu_build(hd.E, "bf16", b * c, d, c, 3, 0, False, "bf16", gpu)
+    _check_balanced(T1, b * c, c)
+    assert np.array_equal(T1, T2) and np.array_equal(C1, C2)
+    # the stored centroids are the means of the members' rows
+    assert np.array_equal(C1, kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), T1, "bf16"))
+
+
+def test_rejects_bad_arguments(gpu):
+    desc = fh.make_desc(1, 64, 4096, 256, "f32", "f32", "f32")
+    ws = torch.empty(16, dtype=torch.uint8, device=gpu)
+    E = torch.zeros(4096 * 64, dtype=torch.float32, device=gpu)
+    cent = torch.empty(256 * 64, dtype=torch.float32, device=gpu)
+    c2t = torch.empty(4096, dtype=torch.int32, device=gpu)
+    with pytest.raises(fh.FlashHeadError) as ei:
+        fh.flashhead_build_clusters(desc, "f32", E, 10, 0, False, cent, c2t, ws)
+    assert ei.value.status == fh.FH_ERR_WORKSPACE
+    big = torch.empty(fh.flashhead_build_clusters_workspace_bytes(desc, "f32"), dtype=torch.uint8, device=gpu)
+    with pytest.raises(fh.FlashHeadError) as ei:
+        fh.flashhead_build_clusters(desc, "f32", E, 0, 0, False, cent, c2t, big)
+    assert ei.value.status == fh.FH_ERR_ARG
