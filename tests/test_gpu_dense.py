@@ -1,0 +1,72 @@
+"""GPU parity of the dense comparator head (flashhead_dense_forward) with the oracle.
+
+The dense head of the FlashHead paper (Section 3: z = E h over the whole vocabulary, then
+argmax or a softmax sample) is what FlashHead replaces; it is the on-GPU baseline of the
+benchmark.  Logits must match the oracle's fp64 values within the stated tolerances; the
+token must match exactly unless the oracle's top-two keys are within their rounding bounds.
+Shapes cover the row GEMV (fp32 and bf16, ragged chunk slots) and the bf16 MFMA path
+(B > 1, d % 32 == 0), greedy and sampling.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from clustered_retrieval_lm_amd import flashhead as fh
+from clustered_retrieval_lm_amd.head import to_device
+from oracle import head as ohead
+from oracle import philox
+
+from . import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # d, V, B, dtype
+    (64, 4096, 4, "f32"),
+    (136, 3000, 1, "bf16"),      # ragged chunk slots
+    (256, 5000, 3, "bf16"),      # B > 1 below the MFMA batch tile
+    (256, 5000, 70, "bf16"),     # MFMA path, ragged batch
+    (96, 2000, 5, "f32"),
+]
+
+
+@pytest.mark.parametrize("d,V,B,dt", CASES)
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_dense_head_matches_the_oracle(gpu, d, V, B, dt, mode):
+    rng = np.random.default_rng(d + V + B)
+    E = workloads.to_storage(rng.standard_normal((V, d)), dt)
+    h = workloads.to_storage(rng.standard_normal((B, d)), dt)
+    tau, seed, step = 0.8, 9, 3
+    desc = fh.make_desc(B, d, V, 1, dt, dt, dt)
+    ws = torch.empty(fh.flashhead_dense_workspace_bytes(desc), dtype=torch.uint8, device=gpu)
+    tok = torch.empty(B, dtype=torch.int32, device=gpu)
+    logits = torch.empty(B, V, dtype=torch.float32, device=gpu)
+    fh.flashhead_dense_forward(desc, to_device(h, gpu), to_device(E, gpu), mode, tau, seed, step, ws, tok, logits)
+    torch.cuda.synchronize()
+    got_z = logits.cpu().numpy().astype(np.float64)
+    got_t = tok.cpu().numpy()
+    ref = ohead.dense_forward(h, dt, E, dt, mode=mode, tau=tau, seed=seed, step=step)
+    L = H.L_mfma(d) if (B > 1 and dt == "bf16" and d % 32 == 0) else H.L_gemv(dt, d)
+    dz = np.abs(got_z - ref.z)
+    assert np.all(dz <= H.gamma(L) * ref.absz + 1e-30), "logit error beyond the rounding bound"
+    if dt == "f32":
+        assert np.all(dz <= 1e-5 * np.maximum(np.abs(ref.z), 1.0))
+    else:
+        assert np.all(dz <= 2e-2)
+    ids = np.arange(V)
+    flagged = 0
+    for r in range(B):
+        G = philox.gumbel(philox.uniform(seed, r, step, 1, ids)) if mode == "sample" else None
+        bnd = H.key_bound(ref.z[r], ref.absz[r], L, mode == "sample", tau, G)
+        key = ref.key[r]
+        order = np.lexsort((ids, -key))
+        t1, t2 = order[0], order[1]
+        if key[t1] - key[t2] <= bnd[t1] + bnd[t2]:
+            flagged += 1                        # near tie: the GPU token must still be a maximum
+            assert key[got_t[r]] >= key[t1] - bnd[t1] - bnd[got_t[r]]
+        else:
+            assert got_t[r] == t1
+    assert flagged <= max(1, B // 10)
