@@ -33,12 +33,16 @@ import numpy as np
 from . import codecs, philox
 
 
-def decode(x: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 values of stored f32 / bf16 arrays."""
+def decode(x, dtype: str) -> np.ndarray:
+    """Exact float64 values of stored f32 / bf16 arrays, or of int4 rows given as the pair
+    (nibbles uint8 [..][d/2], bf16 scale bits [..][d/128])."""
     if dtype == "f32":
         return codecs.f32_to_f64(x)
     if dtype == "bf16":
         return codecs.bf16_to_f64(x)
+    if dtype == "int4":
+        q, sc = x
+        return codecs.int4_dequantize(q, sc)
     raise ValueError(dtype)
 
 

@@ -114,12 +114,17 @@ def objective(En: np.ndarray, a: np.ndarray, c: int) -> float:
     return float(np.sum(1.0 - np.einsum("ij,ij->i", En, Cn[a])))
 
 
-def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str, unit: bool = False) -> np.ndarray:
+def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str, unit: bool = False):
     """Stored centroids of a clustering, rounded once to out_dtype.
 
     unit=False: the mean of each cluster's raw rows (float64 values);
     unit=True:  the normalised sum of the members' normalised rows (Section 3.1's c_k).
+    out_dtype "int4": the stage-1 quantisation of the paper's selective quantisation
+    (Section 4.5, Table 5): the bf16 centroids, quantised per group of 128 like the int4
+    token rows; returns the pair (nibbles [c][d/2], bf16 scale bits [c][d/128]).
     """
+    if out_dtype == "int4":
+        return codecs.int4_quantize(codecs.bf16_to_f64(centroids_from_c2t(E, C2T, "bf16", unit)))
     C2T = np.asarray(C2T, dtype=np.int64)
     c, b = C2T.shape
     cent = np.empty((c, E.shape[1]), dtype=np.float64)

@@ -156,3 +156,23 @@ def test_scored_token_count_matches_the_pages_example():
     scored = res.s.shape[1] + res.z[0].size
     assert scored == fx["scored"]
     assert V // scored == fx["reduction_floor"]          # the page states the ratio as 10x
+
+
+def test_int4_centroids_are_their_dequantised_values():
+    """Selective quantisation of stage 1 (FlashHead paper, Section 4.5, Table 5): the int4
+    centroids act through their exact values q * s; each group keeps |x - q s| <= s / 2."""
+    from oracle import kmeans
+    c, b, d = 40, 4, 256
+    hd = workloads.make_small(d, b * c, c, 2, seed=21, dtype="bf16")
+    C2T = np.arange(b * c).reshape(c, b).astype(np.int32)
+    Cq = kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), C2T, "int4")
+    Cb = kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), C2T, "bf16")
+    deq = ohead.decode(Cq, "int4")
+    s = codecs.bf16_to_f64(Cq[1]).repeat(128, axis=1)
+    assert np.all(np.abs(codecs.bf16_to_f64(Cb) - deq) <= s / 2 + 1e-300)
+    tiles = ohead.pack_tiles(hd.E, "bf16", C2T, "bf16")
+    r4 = ohead.forward(hd.h, "bf16", Cq, "int4", C2T, tiles, 7, mode="sample", tau=0.9, seed=3, step=2)
+    rf = ohead.forward(hd.h, "bf16", deq.astype(np.float32), "f32", C2T, tiles, 7, mode="sample", tau=0.9, seed=3,
+                       step=2)
+    assert np.array_equal(r4.s, rf.s) and np.array_equal(r4.probe_ids, rf.probe_ids)
+    assert np.array_equal(r4.token, rf.token)
