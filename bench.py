@@ -37,9 +37,10 @@ def log(*a):
 
 def algorithmic_bytes(wl, B=1):
     """Bytes a call must read at least: centroids, the kept tiles, their C2T rows, h."""
-    row = {"f32": 4 * wl.d, "bf16": 2 * wl.d, "int4": wl.d // 2 + 2 * (wl.d // 128)}[wl.e_pack]
+    row_of = {"f32": 4 * wl.d, "bf16": 2 * wl.d, "int4": wl.d // 2 + 2 * (wl.d // 128)}
+    row = row_of[wl.e_pack]
     csz = 4 if wl.dtype == "f32" else 2
-    c_bytes = wl.c * wl.d * csz
+    c_bytes = wl.c * row_of[wl.c_dtype]
     tile_bytes = B * wl.p * wl.b * (row + 4)
     return c_bytes, tile_bytes, c_bytes + tile_bytes + B * wl.d * csz
 
@@ -116,13 +117,13 @@ def cpu_baseline(wl, hd, C2T, budget_s=15.0):
     from oracle import head as ohead
     from oracle import kmeans
     Ev = ohead.decode(hd.E, wl.dtype)
-    C = kmeans.centroids_from_c2t(Ev, C2T, wl.dtype)
+    C = kmeans.centroids_from_c2t(Ev, C2T, wl.c_dtype)
     del Ev
     tiles = ohead.pack_tiles(hd.E, wl.dtype, C2T, wl.e_pack)
-    ohead.forward(hd.h, wl.dtype, C, wl.dtype, C2T, tiles, wl.p)          # warm-up
+    ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)        # warm-up
     n, t0 = 0, time.perf_counter()
     while True:
-        ohead.forward(hd.h, wl.dtype, C, wl.dtype, C2T, tiles, wl.p)
+        ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)
         n += 1
         dt = time.perf_counter() - t0
         if dt >= budget_s or n >= 200:
@@ -161,11 +162,11 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fh.load_library()
     wl = workloads.WORKLOADS[args.workload]
-    cfile = "int4" if args.workload == "int4_b16" else args.workload
+    cfile = {"int4_b16": "int4", "gemma_c4": "gemma"}.get(args.workload, args.workload)
     C2T = np.load(os.path.join(ROOT, "tests", "golden", f"clusters_{cfile}.npz"))["C2T"]
     log(f"workload {wl.name}: B={wl.B} d={wl.d} V={wl.V} c={wl.c} p={wl.p} {wl.dtype}/{wl.e_pack}")
     hd = workloads.make_head(wl)
-    dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.dtype, wl.e_pack, wl.dtype,
+    dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.c_dtype, wl.e_pack, wl.dtype,
                                    device="cuda", keep_dense=not args.no_dense)
     c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, wl.B)
     R = args.rotate or max(2, int(np.ceil(4 * MALL_BYTES / max(alg_bytes, 1))))
@@ -308,7 +309,7 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": f"{wl.name} head (B={B}, d={wl.d}, V={wl.V}, c={wl.c}, b={wl.b}, p={p}, "
-                               f"{wl.dtype} C/h, {wl.e_pack} tiles, {args.mode})",
+                               f"{wl.c_dtype} C, {wl.dtype} h, {wl.e_pack} tiles, {args.mode})",
                    "mode": args.mode, "rotated_copies": R},
         "achieved_GBps": round(alg_bytes / t_call / 1e9, 1),
         "algorithmic_bytes": alg_bytes,

@@ -49,7 +49,10 @@ fh_status check_desc(const fh_desc* d, bool need_tiles) {
     return fail(FH_ERR_SHAPE, "c=%lld does not divide V=%lld (clusters must have equal size)",
                 (long long)d->c, (long long)d->V);
   if (d->h_dtype != FH_F32 && d->h_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "h_dtype must be F32 or BF16");
-  if (d->c_dtype != FH_F32 && d->c_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "c_dtype must be F32 or BF16");
+  if (d->c_dtype != FH_F32 && d->c_dtype != FH_BF16 && d->c_dtype != FH_INT4_G128)
+    return fail(FH_ERR_DTYPE, "c_dtype must be F32, BF16 or INT4_G128");
+  if (d->c_dtype == FH_INT4_G128 && d->d % 128 != 0)
+    return fail(FH_ERR_SHAPE, "int4 centroids need d %% 128 == 0 (d=%lld)", (long long)d->d);
   if (d->e_dtype != FH_F32 && d->e_dtype != FH_BF16 && d->e_dtype != FH_INT4_G128)
     return fail(FH_ERR_DTYPE, "e_dtype must be F32, BF16 or INT4_G128");
   if (d->d % 8 != 0) return fail(FH_ERR_SHAPE, "d=%lld must be a multiple of 8", (long long)d->d);
@@ -162,16 +165,43 @@ fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void
   if (!E || !cluster_tokens || !centroids) return fail(FH_ERR_ARG, "E, cluster_tokens and centroids must be non-NULL");
   if (desc->V / desc->c > kMaxTile)
     return fail(FH_ERR_UNSUPPORTED, "cluster size b=%lld exceeds %lld", (long long)(desc->V / desc->c), (long long)kMaxTile);
-  hipError_t e = fh::launch_centroids((int)desc->d, (int)desc->c, (int)(desc->V / desc->c), src_dtype == FH_BF16,
-                                      desc->c_dtype == FH_BF16, unit, E, cluster_tokens, centroids,
-                                      (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "centroids launch");
+  const int c = (int)desc->c, d = (int)desc->d, b = (int)(desc->V / desc->c);
+  hipStream_t hs = (hipStream_t)stream;
+  if (desc->c_dtype != FH_INT4_G128) {
+    hipError_t e = fh::launch_centroids(d, c, b, src_dtype == FH_BF16, desc->c_dtype == FH_BF16, unit, E,
+                                        cluster_tokens, centroids, hs);
+    if (e != hipSuccess) return hip_fail(e, "centroids launch");
+    return FH_OK;
+  }
+  // int4: the bf16 centroids, quantised per group of 128 (a temporary bf16 copy)
+  uint16_t* tmp = nullptr;
+  hipError_t e = hipMalloc(&tmp, (size_t)c * d * sizeof(uint16_t));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  e = fh::launch_centroids(d, c, b, src_dtype == FH_BF16, 1, unit, E, cluster_tokens, tmp, hs);
+  if (e == hipSuccess)
+    e = fh::launch_quant_int4_rows(tmp, c, d, (uint8_t*)centroids,
+                                   (uint16_t*)((char*)centroids + fh::int4_scales_offset(c, d)), hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  hipError_t e2 = hipFree(tmp);
+  if (e != hipSuccess) return hip_fail(e, "int4 centroids");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+  return FH_OK;
+}
+
+fh_status flashhead_centroids_bytes(const fh_desc* desc, size_t* bytes) {
+  fh_status st = check_desc(desc, false);
+  if (st != FH_OK) return st;
+  if (!bytes) return fail(FH_ERR_ARG, "bytes is NULL");
+  const size_t c = (size_t)desc->c, d = (size_t)desc->d;
+  *bytes = desc->c_dtype == FH_F32 ? c * d * 4 : desc->c_dtype == FH_BF16 ? c * d * 2 : fh::int4_rows_bytes(c, d);
   return FH_OK;
 }
 
 static fh_status check_clusters_args(const fh_desc* desc, int32_t src_dtype) {
   fh_status st = check_desc(desc, false);
   if (st != FH_OK) return st;
+  if (desc->c_dtype == FH_INT4_G128)
+    return fail(FH_ERR_DTYPE, "build_clusters stores F32 or BF16 centroids (quantise with flashhead_centroids)");
   if (src_dtype != FH_F32 && src_dtype != FH_BF16) return fail(FH_ERR_DTYPE, "src_dtype must be F32 or BF16");
   if (desc->c > kMaxC) return fail(FH_ERR_UNSUPPORTED, "c=%lld exceeds %lld", (long long)desc->c, (long long)kMaxC);
   if (desc->V / desc->c > kMaxTile)

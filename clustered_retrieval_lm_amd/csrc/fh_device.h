@@ -178,48 +178,6 @@ struct HRegs {
   float v[CH][Fmt<RF>::EPC];
 };
 
-// Load h (fp32 or bf16 storage, d values) into the chunk layout of row format RF with
-// 16-byte loads (d is a multiple of the chunk's value count, so chunks are whole).
-template <int RF, int CH>
-__device__ __forceinline__ void load_h(HRegs<RF, CH>& hr, const void* h, int h_bf16, int d, int lane) {
-  constexpr int EPC = Fmt<RF>::EPC;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int e0 = (lane + kWave * i) * EPC;
-    const bool ok = e0 < d;
-    if (h_bf16) {
-      const uint4* src = reinterpret_cast<const uint4*>((const uint16_t*)h + e0);
-#pragma unroll
-      for (int v = 0; v < EPC / 8; ++v) {
-        const uint4 w = ok ? src[v] : make_uint4(0u, 0u, 0u, 0u);
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          hr.v[i][8 * v + 2 * j] = bf16_lo(ws[j]);
-          hr.v[i][8 * v + 2 * j + 1] = bf16_hi(ws[j]);
-        }
-      }
-      if (EPC % 8) {   // f32 rows (4 values) with bf16 h: one 8-byte load
-        const uint2 w = ok ? *reinterpret_cast<const uint2*>((const uint16_t*)h + e0) : make_uint2(0u, 0u);
-        hr.v[i][0] = bf16_lo(w.x);
-        hr.v[i][1] = bf16_hi(w.x);
-        hr.v[i][2] = bf16_lo(w.y);
-        hr.v[i][3] = bf16_hi(w.y);
-      }
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>((const float*)h + e0);
-#pragma unroll
-      for (int v = 0; v < EPC / 4; ++v) {
-        const uint4 w = ok ? src[v] : make_uint4(0u, 0u, 0u, 0u);
-        hr.v[i][4 * v + 0] = __uint_as_float(w.x);
-        hr.v[i][4 * v + 1] = __uint_as_float(w.y);
-        hr.v[i][4 * v + 2] = __uint_as_float(w.z);
-        hr.v[i][4 * v + 3] = __uint_as_float(w.w);
-      }
-    }
-  }
-}
-
 // h as loaded, before the conversion to fp32: the 16-byte words of each chunk slot (fp32
 // storage fills all W of them, bf16 storage the first half).  Lets a kernel issue the loads
 // of h early and convert after other loads are in flight.
@@ -227,32 +185,29 @@ template <int RF, int CH>
 struct HRaw {
   static constexpr int W = Fmt<RF>::EPC / 4;
   uint4 r[CH][W];
+  uint32_t ok;              // bit i: chunk slot i lies inside h (else it converts to zeros)
 };
 
 template <int RF, int CH>
 __device__ __forceinline__ void load_h_raw(HRaw<RF, CH>& raw, const void* h, int h_bf16, int d, int lane) {
   constexpr int EPC = Fmt<RF>::EPC, W = HRaw<RF, CH>::W;
+  const int esz = h_bf16 ? 2 : 4;
+  // 16-byte words per chunk: all W for fp32 h, W / 2 for bf16 h (a half word when W == 1).
+  // Slots past d read chunk 0 (always inside h) and are zeroed by unpack_h.
+  const int nfull = h_bf16 ? W / 2 : W;
+  raw.ok = 0u;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int e0 = (lane + kWave * i) * EPC;
     const bool ok = e0 < d;
+    raw.ok |= ok ? (1u << i) : 0u;
+    const char* src = (const char*)h + (ok ? (size_t)e0 * esz : 0);
 #pragma unroll
-    for (int v = 0; v < W; ++v) raw.r[i][v] = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) {
-      if (h_bf16) {
-        const uint16_t* src = (const uint16_t*)h + e0;
-        if (EPC >= 8) {
-#pragma unroll
-          for (int v = 0; v < EPC / 8; ++v) raw.r[i][v] = reinterpret_cast<const uint4*>(src)[v];
-        } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(src);
-          raw.r[i][0] = make_uint4(w.x, w.y, 0u, 0u);
-        }
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>((const float*)h + e0);
-#pragma unroll
-        for (int v = 0; v < W; ++v) raw.r[i][v] = src[v];
-      }
+    for (int v = 0; v < W; ++v)
+      if (v < nfull) raw.r[i][v] = reinterpret_cast<const uint4*>(src)[v];
+    if (W == 1 && h_bf16) {
+      const uint2 w = *reinterpret_cast<const uint2*>(src);
+      raw.r[i][0] = make_uint4(w.x, w.y, 0u, 0u);
     }
   }
 }
@@ -262,6 +217,11 @@ __device__ __forceinline__ void unpack_h(HRegs<RF, CH>& hr, const HRaw<RF, CH>& 
   constexpr int EPC = Fmt<RF>::EPC, W = HRaw<RF, CH>::W;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
+    if (!((raw.ok >> i) & 1u)) {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) hr.v[i][e] = 0.f;
+      continue;
+    }
     if (h_bf16) {
       constexpr int NV = EPC >= 8 ? EPC / 8 : 1, NJ = EPC >= 8 ? 4 : 2;
 #pragma unroll
@@ -283,6 +243,15 @@ __device__ __forceinline__ void unpack_h(HRegs<RF, CH>& hr, const HRaw<RF, CH>& 
       }
     }
   }
+}
+
+// Load h (fp32 or bf16 storage, d values) into the chunk layout of row format RF: every
+// 16-byte load is issued before any conversion.
+template <int RF, int CH>
+__device__ __forceinline__ void load_h(HRegs<RF, CH>& hr, const void* h, int h_bf16, int d, int lane) {
+  HRaw<RF, CH> raw;
+  load_h_raw<RF, CH>(raw, h, h_bf16, d, lane);
+  unpack_h<RF, CH>(hr, raw, h_bf16);
 }
 
 // Partial dot of one 16-byte chunk with h (scale applies to int4 only).

@@ -62,6 +62,12 @@ hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int
 size_t build_clusters_workspace_bytes(int V, int d, int c);
 hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* E, int iters, uint64_t seed, int unit,
                                  int dst_bf16, void* centroids, int32_t* c2t, void* ws, hipStream_t st);
+// int4 rows ([rows][d/2] nibbles) followed by their bf16 group scales ([rows][d/128]) in one
+// buffer: the scales start at this byte offset.
+inline size_t int4_scales_offset(size_t rows, size_t d) { return (rows * d / 2 + 255) & ~(size_t)255; }
+inline size_t int4_rows_bytes(size_t rows, size_t d) { return int4_scales_offset(rows, d) + rows * (d / 128) * 2; }
+hipError_t launch_quant_int4_rows(const uint16_t* src, int rows, int d, uint8_t* q, uint16_t* scales,
+                                  hipStream_t st);
 hipError_t launch_pack(int V, int d, int c, int b, int src_bf16, int dst_fmt, const void* E,
                        const int32_t* c2t, void* tiles, uint16_t* scales, uint32_t* counts,
                        uint32_t* bad, hipStream_t st);

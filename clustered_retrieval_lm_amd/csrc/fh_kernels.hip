@@ -41,7 +41,7 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
 template <int RF, int CH, int NR = kRPI>
 struct RowGroup {
   uint4 w[NR][CH];
-  float sc[NR][CH];
+  uint32_t sc[NR][CH];      // int4: bf16 bits of the group scale (converted at the dot)
 };
 
 // Load rows [j0, j0 + NR) (those < nrows) of a matrix with row stride rb bytes.
@@ -57,7 +57,7 @@ __device__ __forceinline__ void rows_load(RowGroup<RF, CH, NR>& g, const char* b
       const int q = lane + kWave * i;
       const bool ok = j < nrows && q < cpr;
       g.w[r][i] = ok ? ld16_stream(base + (size_t)j * rb + (size_t)q * 16) : make_uint4(0u, 0u, 0u, 0u);
-      g.sc[r][i] = (RF == RF_INT4 && ok) ? bf16_to_f32(scales[(size_t)j * spr + (q >> 2)]) : 0.f;
+      g.sc[r][i] = (RF == RF_INT4 && ok) ? (uint32_t)scales[(size_t)j * spr + (q >> 2)] : 0u;
     }
   }
 }
@@ -69,7 +69,7 @@ __device__ __forceinline__ void rows_dot(const RowGroup<RF, CH, NR>& g, const HR
   for (int r = 0; r < NR; ++r) {
     float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) acc = chunk_dot<RF>(g.w[r][i], hr.v[i], acc, g.sc[r][i]);
+    for (int i = 0; i < CH; ++i) acc = chunk_dot<RF>(g.w[r][i], hr.v[i], acc, __uint_as_float(g.sc[r][i] << 16));
     out[r] = wave_sum(acc);
   }
 }
@@ -79,6 +79,7 @@ __device__ __forceinline__ void rows_dot(const RowGroup<RF, CH, NR>& g, const HR
 struct ScoreParams {
   const void* h;
   const char* C;
+  const uint16_t* c_scales;   // int4 centroids: their bf16 group scales
   int h_bf16, B, c, d;
   int sample;
   float tau;
@@ -96,11 +97,17 @@ __global__ __launch_bounds__(kThreads) void k_scores_gemv(ScoreParams a) {
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int rb = row_bytes_of(RF, a.d);
+  // h and the first rows are requested together; h is converted once both are in flight
+  HRaw<RF, CH> hraw;
+  load_h_raw<RF, CH>(hraw, (const char*)a.h + (size_t)r * a.d * (a.h_bf16 ? 2 : 4), a.h_bf16, a.d, lane);
+  const int kfirst = wg * kRPI;
+  RowGroup<RF, CH> g;
+  if (kfirst < a.c) rows_load<RF, CH>(g, a.C, rb, kfirst, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
   HRegs<RF, CH> hr;
-  load_h<RF, CH>(hr, (const char*)a.h + (size_t)r * a.d * (a.h_bf16 ? 2 : 4), a.h_bf16, a.d, lane);
-  for (int k0 = wg * kRPI; k0 < a.c; k0 += nw * kRPI) {
-    RowGroup<RF, CH> g;
-    rows_load<RF, CH>(g, a.C, rb, k0, a.c, nullptr, 0, lane);
+  unpack_h<RF, CH>(hr, hraw, a.h_bf16);
+  for (int k0 = kfirst; k0 < a.c; k0 += nw * kRPI) {
+    if (k0 != kfirst)
+      rows_load<RF, CH>(g, a.C, rb, k0, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
     float s[kRPI];
     rows_dot<RF, CH>(g, hr, s);
 #pragma unroll
@@ -566,6 +573,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
 struct B1Params {
   const void* h;
   const char* C;
+  const uint16_t* c_scales;   // int4 centroids: their bf16 group scales
   int h_bf16, c, d, b, p;
   int cpad;             // keys padded with NaN up to this count
   int sample;
@@ -591,11 +599,17 @@ __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
   const int rb = row_bytes_of(RF, a.d);
+  // h and the first rows are requested together; h is converted once both are in flight
+  HRaw<RF, CH> hraw;
+  load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
+  const int kfirst = wg * kRPI;
+  RowGroup<RF, CH> g;
+  if (kfirst < a.c) rows_load<RF, CH>(g, a.C, rb, kfirst, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
   HRegs<RF, CH> hr;
-  load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  for (int k0 = wg * kRPI; k0 < a.c; k0 += nw * kRPI) {
-    RowGroup<RF, CH> g;
-    rows_load<RF, CH>(g, a.C, rb, k0, a.c, nullptr, 0, lane);
+  unpack_h<RF, CH>(hr, hraw, a.h_bf16);
+  for (int k0 = kfirst; k0 < a.c; k0 += nw * kRPI) {
+    if (k0 != kfirst)
+      rows_load<RF, CH>(g, a.C, rb, k0, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
     float s[kRPI];
     rows_dot<RF, CH>(g, hr, s);
 #pragma unroll
@@ -1211,6 +1225,30 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams a) {
   }
 }
 
+// Rows [rows][d] of bf16 values to int4 groups of 128 (the k_pack rule): nibbles
+// [rows][d/2] and bf16 scales [rows][d/128].  One wave per row.
+__global__ __launch_bounds__(kThreads) void k_quant_int4_rows(const uint16_t* src, int rows, int d, uint8_t* q,
+                                                              uint16_t* scales) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t* x = src + (size_t)row * d;
+  const int ng = d >> 7;
+  for (int gi = 0; gi < ng; ++gi) {
+    const float x0 = bf16_to_f32(x[gi * 128 + 2 * lane]), x1 = bf16_to_f32(x[gi * 128 + 2 * lane + 1]);
+    const float amax = wave_max_f32(fmaxf(fabsf(x0), fabsf(x1)));
+    const uint16_t sb = f32_to_bf16_rne(amax / 7.0f);
+    const float s = bf16_to_f32(sb);
+    int q0 = 0, q1 = 0;
+    if (s != 0.f) {
+      q0 = (int)fminf(fmaxf(rintf(x0 / s), -7.f), 7.f);
+      q1 = (int)fminf(fmaxf(rintf(x1 / s), -7.f), 7.f);
+    }
+    q[(size_t)row * (d / 2) + gi * 64 + lane] = (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
+    if (lane == 0) scales[(size_t)row * ng + gi] = sb;
+  }
+}
+
 __global__ void k_check_counts(const uint32_t* counts, int V, uint32_t* bad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < V && counts[i] != 1u) atomicOr(bad, 2u);
@@ -1400,16 +1438,20 @@ static hipError_t launch_mfma(const MfmaParams& p, int max_wg, hipStream_t st) {
 hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const Sampling& smp,
                          const Workspace& ws, float* keys_out, hipStream_t st) {
   const Rng rng = make_rng(smp.seed, smp.step);
+  const uint16_t* c_scales =
+      s.c_fmt == RF_INT4 ? (const uint16_t*)((const char*)C + int4_scales_offset(s.c, s.d)) : nullptr;
   if (s.B == 1) {   // the same kernel the fused B = 1 forward runs
     B1Params a{};
-    a.h = h; a.C = (const char*)C; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
+    a.h = h; a.C = (const char*)C; a.c_scales = c_scales; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
     a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
     a.keys = ws.keys; a.keys_out = keys_out; a.cpad = b1_key_slots(s.c) * kB1Threads;
     const int ch = chunk_slots(s.c_fmt, s.d);
     if (s.c_fmt == RF_F32) {
       FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
-    } else {
+    } else if (s.c_fmt == RF_BF16) {
       FH_DISPATCH_CH(ch, (launch_b1_scores<RF_BF16, kCH>(a, s.c, st)));
+    } else {
+      FH_DISPATCH_CH_INT4(ch, (launch_b1_scores<RF_INT4, kCH>(a, s.c, st)));
     }
     return hipGetLastError();
   }
@@ -1422,7 +1464,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     p.keys = ws.keys; p.keys_out = keys_out; p.mask = ws.mask; p.W = ws.W;
     return launch_mfma<EPI_KEYS>(p, 1 << 30, st);
   }
-  ScoreParams a{h, (const char*)C, s.h_bf16, s.B, s.c, s.d, smp.sample, smp.tau, rng,
+  ScoreParams a{h, (const char*)C, c_scales, s.h_bf16, s.B, s.c, s.d, smp.sample, smp.tau, rng,
                 ws.keys, keys_out, ws.mask, ws.W};
   const int groups = (s.c + kRPI - 1) / kRPI;
   int wgs = (groups + 3) / 4;
@@ -1431,8 +1473,10 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
   const int ch = chunk_slots(s.c_fmt, s.d);
   if (s.c_fmt == RF_F32) {
     FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_scores_gemv<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a));
-  } else {
+  } else if (s.c_fmt == RF_BF16) {
     FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_scores_gemv<RF_BF16, kCH>), grid, dim3(kThreads), 0, st, a));
+  } else {
+    FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_scores_gemv<RF_INT4, kCH>), grid, dim3(kThreads), 0, st, a));
   }
   return hipGetLastError();
 }
@@ -1527,6 +1571,12 @@ hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int
                             const int32_t* c2t, void* out, hipStream_t st) {
   CentroidParams a{(const char*)E, c2t, out, d, b, src_bf16, dst_bf16, unit};
   hipLaunchKernelGGL(k_centroids, dim3(c), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_int4_rows(const uint16_t* src, int rows, int d, uint8_t* q, uint16_t* scales,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(k_quant_int4_rows, dim3((rows + 3) / 4), dim3(kThreads), 0, st, src, rows, d, q, scales);
   return hipGetLastError();
 }
 

@@ -65,6 +65,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_workspace_bytes": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_pack": ([D, i32, vp, vp, vp, vp, vp], ctypes.c_int),
         "flashhead_centroids": ([D, i32, vp, vp, i32, vp, vp], ctypes.c_int),
+        "flashhead_centroids_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_build_clusters_workspace_bytes": ([D, i32, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_build_clusters": ([D, i32, vp, i32, u64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "flashhead_centroid_scores": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp], ctypes.c_int),
@@ -161,6 +162,12 @@ def flashhead_centroids(desc: fh_desc, src_dtype, E, cluster_tokens, centroids, 
     src = DTYPES[src_dtype] if isinstance(src_dtype, str) else int(src_dtype)
     _check(load_library().flashhead_centroids(ctypes.byref(desc), src, _ptr(E), _ptr(cluster_tokens), int(bool(unit)),
                                               _ptr(centroids), _stream(stream)))
+
+
+def flashhead_centroids_bytes(desc: fh_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().flashhead_centroids_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
 
 
 def flashhead_build_clusters_workspace_bytes(desc: fh_desc, src_dtype) -> int:

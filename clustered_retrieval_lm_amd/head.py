@@ -53,8 +53,8 @@ class DeviceHead:
         """Build the head from a clustering alone: centroids computed on the GPU."""
         Ed = to_device(E, device)
         c2t_d = to_device(np.asarray(c2t, dtype=np.int32), device)
-        cent = torch.empty(c * d * (2 if c_dtype == "bf16" else 4), dtype=torch.uint8, device=device)
         desc = fh.make_desc(1, d, V, c, h_dtype, c_dtype, e_dtype)
+        cent = torch.empty(fh.flashhead_centroids_bytes(desc), dtype=torch.uint8, device=device)
         fh.flashhead_centroids(desc, e_src, Ed, c2t_d, cent, unit=unit, stream=stream)
         return cls(d, V, c, cent, c2t_d, Ed, e_src, c_dtype, e_dtype, h_dtype, device, keep_dense, stream)
 

@@ -77,7 +77,7 @@ typedef struct fh_desc {
     int64_t V;               /* vocabulary size */
     int64_t c;               /* clusters; b = V / c tokens per cluster */
     int32_t h_dtype;         /* FH_F32 | FH_BF16 */
-    int32_t c_dtype;         /* FH_F32 | FH_BF16 (centroids) */
+    int32_t c_dtype;         /* FH_F32 | FH_BF16 | FH_INT4_G128 (centroids) */
     int32_t e_dtype;         /* FH_F32 | FH_BF16 | FH_INT4_G128 (token embeddings / tiles) */
     int32_t reserved;        /* must be 0 */
 } fh_desc;
@@ -137,6 +137,7 @@ fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E,
  * library's readings.  All arithmetic is fp64 with fixed reduction orders and stable
  * sorts, so the result does not depend on scheduling.
  *   desc           V, d, c (b = V / c <= 256, c <= 32768); desc->c_dtype: stored centroids
+ *                  (F32 | BF16)
  *   src_dtype      dtype of E (F32 | BF16)
  *   E              device, [V][d] token-major embeddings
  *   iters          >= 1 rounds
@@ -154,15 +155,25 @@ fh_status flashhead_build_clusters(const fh_desc* desc, int32_t src_dtype, const
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of the centroid buffer for desc->c_dtype: c d 4 (F32), c d 2 (BF16), or for
+ * INT4_G128 (the paper's stage-1 quantisation, Section 4.5, Table 5) the nibbles
+ * [c][d/2] (element 2i in the low nibble of byte i) followed, at byte offset
+ * round_up(c d / 2, 256), by the bf16 group scales [c][d/128].  Writes it to *bytes.
+ */
+fh_status flashhead_centroids_bytes(const fh_desc* desc, size_t* bytes);
+
+/*
  * Offline centroids of a given clustering (Section 3.1, "Centroid matrix").
  *   E              device, [V][d] token-major embeddings of dtype src_dtype (F32 | BF16)
  *   cluster_tokens device, int32 [c][b]: C2T
  *   unit           0: C[k] = mean of the b rows of cluster k;
  *                  1: C[k] = normalise(sum of the normalised rows), the unit centroid the
  *                     paper stores (a zero row or sum contributes / gives 0)
- *   centroids      device out, [c][d] in desc->c_dtype
+ *   centroids      device out, [c][d] in desc->c_dtype (layout: flashhead_centroids_bytes)
  * Sums run in fp64 and are rounded once to the output dtype (bf16: nearest even).  The
- * forward pass accepts either form.  Asynchronous on `stream`.
+ * forward pass accepts either form.  INT4_G128: the bf16 centroids, quantised per group of
+ * 128 exactly like int4 token rows (s = bf16(amax / 7), q = clamp(rne(x / s), -7, 7)); this
+ * case allocates a temporary buffer and synchronises `stream`.  Otherwise asynchronous.
  */
 fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void* E,
                               const int32_t* cluster_tokens, int32_t unit, void* centroids,
@@ -173,7 +184,7 @@ fh_status flashhead_centroids(const fh_desc* desc, int32_t src_dtype, const void
  * turned into probe keys -- s (greedy) or s / tau + G(U(seed, r, step, 0, k)) (sampling) --
  * stored in the workspace and, if keys_out (device, float [B][c]) is non-NULL, there too.
  *   h         device [B][d], desc->h_dtype
- *   centroids device [c][d], desc->c_dtype
+ *   centroids device [c][d], desc->c_dtype (INT4_G128 layout: flashhead_centroids_bytes)
  */
 fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const void* centroids,
                                     int32_t mode, float temperature, uint64_t seed, uint64_t step,
@@ -223,7 +234,7 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
  * The whole head: stage 1, probe selection and stage 2 as above, enqueued back to back
  * (flashhead_centroid_scores, then flashhead_select_and_probe).
  *   h              device [B][d]
- *   centroids      device [c][d]
+ *   centroids      device [c][d] in desc->c_dtype (INT4_G128 layout: flashhead_centroids_bytes)
  *   cluster_tokens device int32 [c][b]
  *   E_tiles        device, cluster-major tiles (flashhead_pack)
  *   E_scales       device, INT4_G128 scales, else NULL

@@ -85,7 +85,20 @@ def _c2t(name: str) -> np.ndarray:
 
 
 def cluster_file(name: str) -> str:
-    return "int4" if name == "int4_b16" else name
+    return {"int4_b16": "int4", "gemma_c4": "gemma"}.get(name, name)
+
+
+def centroid_buffer(C, c_dtype: str) -> np.ndarray:
+    """Stored centroids as the library takes them: f32 / bf16 arrays as they are; int4 as
+    one byte buffer (nibbles [c][d/2], then from round_up(c d / 2, 256) the bf16 scales)."""
+    if c_dtype != "int4":
+        return C
+    q, sc = C
+    off = (q.size + 255) // 256 * 256
+    buf = np.zeros(off + sc.size * 2, dtype=np.uint8)
+    buf[:q.size] = q.reshape(-1)
+    buf[off:] = np.ascontiguousarray(sc, dtype=np.uint16).reshape(-1).view(np.uint8)
+    return buf
 
 
 @functools.lru_cache(maxsize=4)
@@ -94,7 +107,7 @@ def load(name: str):
     wl = workloads.WORKLOADS[name]
     hd = workloads.make_head(wl)
     C2T = _c2t(cluster_file(name))
-    C = kmeans.centroids_from_c2t(ohead.decode(hd.E, wl.dtype), C2T, wl.dtype)
+    C = kmeans.centroids_from_c2t(ohead.decode(hd.E, wl.dtype), C2T, wl.c_dtype)
     return wl, hd, C2T, C
 
 

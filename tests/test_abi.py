@@ -59,7 +59,8 @@ def _ws(desc, p):
     (dict(B=1, d=1150, V=262144, c=16384), fh.FH_ERR_SHAPE),          # d % 8
     (dict(B=1, d=1160, V=262144, c=16384, e_dtype="int4"), fh.FH_ERR_SHAPE),   # int4 needs d % 128
     (dict(B=1, d=1152, V=262144, c=16384, h_dtype=7), fh.FH_ERR_DTYPE),
-    (dict(B=1, d=1152, V=262144, c=16384, c_dtype=fh.FH_INT4_G128), fh.FH_ERR_DTYPE),
+    (dict(B=1, d=1152, V=262144, c=16384, c_dtype=7), fh.FH_ERR_DTYPE),
+    (dict(B=1, d=1160, V=262144, c=16384, c_dtype=fh.FH_INT4_G128), fh.FH_ERR_SHAPE),  # int4 centroids: d % 128
     (dict(B=1, d=8192, V=262144, c=16384), fh.FH_ERR_UNSUPPORTED),    # bf16 rows limited to d <= 4096
     (dict(B=1, d=1152, V=65536 * 16, c=65536), fh.FH_ERR_UNSUPPORTED),  # c > 32768
     (dict(B=1, d=1152, V=512 * 300, c=300), fh.FH_ERR_UNSUPPORTED),   # b > 256

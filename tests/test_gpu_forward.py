@@ -107,17 +107,39 @@ def test_small_heads(gpu, d, b, c, B, p, dt, et, mode):
     print(rep)
 
 
+# ------------------------------------------------------------------ int4 centroids (stage 1)
+# The paper's selective quantisation (Section 4.5, Table 5): stage 1 on int4 centroids,
+# stage 2 on the bf16 tiles.
+
+@pytest.mark.parametrize("B", [1, 5])
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_small_heads_int4_centroids(gpu, B, mode):
+    d, b, c, p = 256, 16, 777, 40
+    hd = workloads.make_small(d, b * c, c, B, seed=77 + B, sigma_c=1.0, sigma_n=0.5, dtype="bf16")
+    C2T = H.latent_clusters(hd.latent, c)
+    C = kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), C2T, "int4")
+    dev = DeviceHead(d, b * c, c, H.centroid_buffer(C, "int4"), C2T, hd.E, "bf16", "int4", "bf16", "bf16",
+                     device=gpu)
+    tiles = ohead.pack_tiles(hd.E, "bf16", C2T, "bf16")
+    rep = H.Report()
+    for step in (range(3) if mode == "sample" else [0]):
+        _run_and_compare(dev, hd.h, "bf16", C, C2T, tiles, p, mode, 0.9, 5, step, False, rep)
+    print(rep)
+
+
 # ------------------------------------------------------------------ full-size heads
 
 FULL = [("llama", "greedy", 1.0), ("gemma", "greedy", 1.0), ("gemma", "sample", 1.0),
         ("qwen", "greedy", 1.0), ("qwen", "sample", 0.8), ("int4", "greedy", 1.0), ("int4", "sample", 1.0),
-        ("int4_b16", "greedy", 1.0), ("int4_b16", "sample", 1.0)]
+        ("int4_b16", "greedy", 1.0), ("int4_b16", "sample", 1.0), ("gemma_c4", "greedy", 1.0),
+        ("gemma_c4", "sample", 1.0)]
 
 
 @pytest.mark.parametrize("name,mode,tau", FULL)
 def test_full_size(gpu, name, mode, tau):
     wl, hd, C2T, C = H.load(name)
-    dev = DeviceHead(wl.d, wl.V, wl.c, C, C2T, hd.E, wl.dtype, wl.dtype, wl.e_pack, wl.dtype, device=gpu)
+    dev = DeviceHead(wl.d, wl.V, wl.c, H.centroid_buffer(C, wl.c_dtype), C2T, hd.E, wl.dtype, wl.c_dtype, wl.e_pack,
+                     wl.dtype, device=gpu)
     tiles = H.oracle_tiles(name)
     rep = H.Report()
     steps = [0] if mode == "greedy" else [0, 1, 7, 123, 999]

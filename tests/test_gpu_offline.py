@@ -95,3 +95,28 @@ def test_pack_rejects_non_permutation(gpu):
     with pytest.raises(fh.FlashHeadError) as ei:
         fh.flashhead_pack(fh.make_desc(1, d, c * b, c, "f32", "f32", "f32"), "f32", E, to_device(C2T, gpu), tiles)
     assert ei.value.status == fh.FH_ERR_ARG
+
+
+@pytest.mark.parametrize("unit", [False, True])
+def test_int4_centroids_bit_exact(gpu, unit):
+    """Stage-1 int4 centroids (selective quantisation, FlashHead paper Section 4.5): the bf16
+    centroids quantised per group of 128; the oracle's rounding of the fp64 sums to bf16
+    is exact, so the nibbles and scales must match bit for bit (unit: within one bf16 ulp
+    before quantisation, so only the mean form is compared exactly)."""
+    d, c, b = 384, 211, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=9, dtype="bf16")
+    C2T = H.latent_clusters(hd.latent, c)
+    desc = fh.make_desc(1, d, b * c, c, "bf16", "int4", "bf16")
+    buf = torch.empty(fh.flashhead_centroids_bytes(desc), dtype=torch.uint8, device=gpu)
+    fh.flashhead_centroids(desc, "bf16", to_device(hd.E, gpu), to_device(np.asarray(C2T, np.int32), gpu), buf,
+                           unit=unit)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    q, sc = kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), C2T, "int4", unit=unit)
+    off = (q.size + 255) // 256 * 256                       # the bytes in between are padding
+    assert got.size == off + sc.size * 2
+    got_q, got_s = got[:q.size].reshape(q.shape), got[off:].view(np.uint16).reshape(sc.shape)
+    if not unit:
+        assert np.array_equal(got_q, q) and np.array_equal(got_s, sc)
+    else:
+        assert np.mean(got_q == q) > 0.99 and np.mean(got_s == sc) > 0.99

@@ -48,14 +48,19 @@ class Workload:
     sample_seed: int = 1  # Philox key for the sampler
     data_seed: int = 0    # PCG64 seed of the generator and k-means++ key
     kmeans_iters: int = 10
+    c_pack: str = ""      # stored centroid dtype when it differs from dtype ("int4")
 
     @property
     def b(self) -> int:
         return self.V // self.c
 
+    @property
+    def c_dtype(self) -> str:
+        return self.c_pack or self.dtype
+
 
 # The five head shapes.  B for "int4" is 1 in the headline configuration; the
-# batched variant (B=16) is "int4_b16".
+# batched variant (B=16) is "int4_b16"; "gemma_c4" is the Gemma shape with int4 centroids.
 WORKLOADS = {
     "tiny": Workload("tiny", d=64, V=4096, c=256, B=4, p=8, sigma_c=1.0, sigma_n=0.3,
                      dtype="f32", e_pack="f32", temperatures=(1.0,)),
@@ -69,6 +74,9 @@ WORKLOADS = {
                      dtype="bf16", e_pack="int4", temperatures=(1.0,)),
     "int4_b16": Workload("int4_b16", d=3072, V=128256, c=8016, B=16, p=256, sigma_c=0.02,
                          sigma_n=0.01, dtype="bf16", e_pack="int4", temperatures=(1.0,)),
+    # the Gemma head with int4 stage-1 centroids and bf16 tiles (selective quantisation)
+    "gemma_c4": Workload("gemma_c4", d=1152, V=262144, c=16384, B=1, p=512, sigma_c=0.02, sigma_n=0.01,
+                         dtype="bf16", e_pack="bf16", temperatures=(1.0,), c_pack="int4"),
 }
 
 
