@@ -12,12 +12,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libflashhead.so")
-SOURCES = ["fh_kernels.hip", "fh_cluster.hip", "fh_api.hip"]
-HEADERS = ["fh_device.h", "fh_internal.h"]
+SOURCES = ["fh_kernels.hip", "fh_cluster.hip", "fh_mc.hip", "fh_api.hip"]
+HEADERS = ["fh_device.h", "fh_internal.h", "fh_select.h"]
 ARCH = os.environ.get("FLASHHEAD_ARCH", "gfx950")
 
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-O3", "-std=c++17", "-fPIC",
     f"--offload-arch={ARCH}",
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,19 +32,46 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIB; returns its path.  Always recompiles."""
-    os.makedirs(LIBDIR, exist_ok=True)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _run(cmd: list) -> subprocess.Popen:
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _messages(out: str) -> list:
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless.
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    return [ln for ln in out.splitlines() if noise not in ln]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel) and link LIB; returns its path.  Always recompiles."""
+    os.makedirs(LIBDIR, exist_ok=True)
+    objdir = os.path.join(LIBDIR, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    objs, procs = [], []
+    for s in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
+        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append((s, _run(cmd)))
+    failed, msgs = [], []
+    for s, pr in procs:
+        out, _ = pr.communicate()
+        m = _messages(out)
+        if pr.returncode != 0:
+            failed.append(s)
+        msgs += m
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}:\n" + "\n".join(msgs))
+    tmp = LIB + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
+    msgs += _messages(res.stdout + res.stderr)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError("link failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
     os.replace(tmp, LIB)

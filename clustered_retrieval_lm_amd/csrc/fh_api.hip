@@ -33,6 +33,7 @@ fh_status hip_fail(hipError_t e, const char* what) {
 constexpr int64_t kMaxC = 32768;
 constexpr int64_t kMaxB = 65535;
 constexpr int64_t kMaxTile = 256;
+constexpr int64_t kMaxSets = (int64_t(1) << 31) - 1;
 
 int fmt_of(int32_t dt) { return dt == FH_F32 ? fh::RF_F32 : dt == FH_BF16 ? fh::RF_BF16 : fh::RF_INT4; }
 
@@ -342,6 +343,47 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
   hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
   return select_and_probe(s, (int)p, h, cluster_tokens, E_tiles, E_scales, smp, ws, out, hs);
+}
+
+fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* bytes) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if (!bytes) return fail(FH_ERR_ARG, "bytes is NULL");
+  *bytes = fh::carve_mc_workspace(nullptr, (int)desc->B, (int)desc->c, (int)(desc->V / desc->c)).bytes;
+  return FH_OK;
+}
+
+fh_status flashhead_mc_marginal(const fh_desc* desc, const void* h, const void* centroids,
+                                const int32_t* cluster_tokens, const void* E_tiles, const void* E_scales, int64_t p,
+                                float temperature, uint64_t seed, int64_t n_sets, int32_t clip, void* workspace,
+                                size_t workspace_bytes, double* out, void* stream) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if ((st = check_sampling(FH_SAMPLE, temperature)) != FH_OK) return st;
+  if (!h || !centroids || !cluster_tokens || !E_tiles || !out)
+    return fail(FH_ERR_ARG, "h, centroids, cluster_tokens, E_tiles and out must be non-NULL");
+  if (desc->e_dtype == FH_INT4_G128 && !E_scales) return fail(FH_ERR_ARG, "E_scales must be non-NULL for INT4_G128");
+  if (n_sets < 1 || n_sets > kMaxSets)
+    return fail(FH_ERR_ARG, "n_sets=%lld must satisfy 1 <= n_sets <= %lld", (long long)n_sets, (long long)kMaxSets);
+  if (clip != 0 && clip != 1) return fail(FH_ERR_ARG, "clip must be 0 or 1");
+  const fh::HeadShape s = shape_of(desc);
+  const fh::McWorkspace w = fh::carve_mc_workspace(workspace, s.B, s.c, s.b);
+  if (!workspace) return fail(FH_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < w.bytes)
+    return fail(FH_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
+                w.bytes);
+  hipStream_t hs = (hipStream_t)stream;
+  // every logit of the head: the forward pass with p = c, greedy (its keys are the logits)
+  const fh::Sampling plain = sampling_of(FH_GREEDY, 1.0f, 0, 0);
+  hipError_t e = fh::launch_scores(s, h, centroids, plain, w.fw, w.s, hs);
+  if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
+  const fh_outputs all{w.token, nullptr, w.z, nullptr};
+  if ((st = select_and_probe(s, s.c, h, cluster_tokens, E_tiles, E_scales, plain, w.fw, &all, hs)) != FH_OK)
+    return st;
+  e = fh::launch_mc(s, (int)p, temperature, seed, n_sets, clip, cluster_tokens, w, out, hs);
+  if (e != hipSuccess) return hip_fail(e, "Monte-Carlo marginal launch");
+  return FH_OK;
 }
 
 fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes) {

@@ -401,13 +401,14 @@ struct KmWs {
 
 size_t cub_tmp_bytes(int V, int c) {
   size_t s1 = 0, s2 = 0, s3 = 0, s4 = 0;
-  hipcub::DeviceRadixSort::SortPairsDescending(nullptr, s1, (const uint64_t*)nullptr, (uint64_t*)nullptr,
-                                               (const int32_t*)nullptr, (int32_t*)nullptr, V);
-  hipcub::DeviceRadixSort::SortPairs(nullptr, s2, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                     (const int32_t*)nullptr, (int32_t*)nullptr, V);
-  hipcub::DeviceScan::ExclusiveSum(nullptr, s3, (const int32_t*)nullptr, (int32_t*)nullptr, c);
-  hipcub::DeviceSelect::Flagged(nullptr, s4, hipcub::CountingInputIterator<int32_t>(0), (const uint8_t*)nullptr,
-                                (int32_t*)nullptr, (int32_t*)nullptr, V);
+  // size queries only (null temporary storage): nothing is launched
+  (void)hipcub::DeviceRadixSort::SortPairsDescending(nullptr, s1, (const uint64_t*)nullptr, (uint64_t*)nullptr,
+                                                     (const int32_t*)nullptr, (int32_t*)nullptr, V);
+  (void)hipcub::DeviceRadixSort::SortPairs(nullptr, s2, (const int32_t*)nullptr, (int32_t*)nullptr,
+                                           (const int32_t*)nullptr, (int32_t*)nullptr, V);
+  (void)hipcub::DeviceScan::ExclusiveSum(nullptr, s3, (const int32_t*)nullptr, (int32_t*)nullptr, c);
+  (void)hipcub::DeviceSelect::Flagged(nullptr, s4, hipcub::CountingInputIterator<int32_t>(0),
+                                      (const uint8_t*)nullptr, (int32_t*)nullptr, (int32_t*)nullptr, V);
   return std::max(std::max(s1, s2), std::max(s3, s4));
 }
 

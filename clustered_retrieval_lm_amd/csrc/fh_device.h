@@ -66,10 +66,14 @@ __host__ __device__ inline Rng make_rng(uint64_t seed, uint64_t step) {
   return Rng{(uint32_t)seed, (uint32_t)(seed >> 32), (uint32_t)step, (uint32_t)((step >> 32) << 2)};
 }
 
+// The four words of block n4 of (row, stream): the words of elements 4 n4 .. 4 n4 + 3.
+__host__ __device__ __forceinline__ uint4 rng_block(const Rng& g, uint32_t row, uint32_t stream, uint32_t n4) {
+  return philox4x32_10(make_uint4(n4, row, g.step_lo, g.step_hi4 | stream), g.k0, g.k1);
+}
+
 // The word for element n of (row, stream).
 __host__ __device__ __forceinline__ uint32_t rng_word(const Rng& g, uint32_t row, uint32_t stream, uint32_t n) {
-  uint4 ctr = make_uint4(n >> 2, row, g.step_lo, g.step_hi4 | stream);
-  uint4 o = philox4x32_10(ctr, g.k0, g.k1);
+  const uint4 o = rng_block(g, row, stream, n >> 2);
   const uint32_t s = n & 3u;
   return s == 0 ? o.x : s == 1 ? o.y : s == 2 ? o.z : o.w;
 }
@@ -84,10 +88,14 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 // Probe or token key: the logit itself (greedy) or logit / tau + Gumbel noise (sampling).
 // Adding +0 turns a -0 key into +0 (round to nearest), so keys compare the same as floats
 // and as ord_key values.
+__device__ __forceinline__ float sample_key(float z, float tau, uint32_t word) {
+  return z / tau + gumbel(word_to_uniform(word)) + 0.0f;
+}
+
 __device__ __forceinline__ float make_key(float z, int sample, float tau, const Rng& g, uint32_t row,
                                           uint32_t stream, uint32_t n) {
   if (!sample) return z + 0.0f;
-  return z / tau + gumbel(word_to_uniform(rng_word(g, row, stream, n))) + 0.0f;
+  return sample_key(z, tau, rng_word(g, row, stream, n));
 }
 
 // ---------------------------------------------------------------- wave reductions

@@ -58,6 +58,24 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
                         uint64_t* best, int32_t* token, float* logits, hipStream_t st);
 hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int unit, const void* E,
                             const int32_t* c2t, void* out, hipStream_t st);
+// Monte-Carlo marginal (fh_mc.hip): the forward workspace for p = c, then the centroid
+// logits s, all token logits z (tile order), the per-cluster softmax statistics M and Zc,
+// the accumulated weights A, the per-row minimum cell and the forward's token output.
+struct McWorkspace {
+  Workspace fw;
+  float* s;           // [B][c]
+  float* z;           // [B][c][b]
+  double* M;          // [B][c]
+  double* Zc;         // [B][c]
+  double* A;          // [B][c]
+  uint64_t* minneg;   // [B]
+  int32_t* token;     // [B]
+  size_t bytes;
+};
+McWorkspace carve_mc_workspace(void* base, int B, int c, int b);
+// Reads w.s and w.z (written by the forward path) and writes out[B][V].
+hipError_t launch_mc(const HeadShape& s, int p, float tau, uint64_t seed, int64_t n_sets, int clip,
+                     const int32_t* c2t, const McWorkspace& w, double* out, hipStream_t st);
 // Offline balanced spherical k-means (fh_cluster.hip); synchronises `st` once per round.
 size_t build_clusters_workspace_bytes(int V, int d, int c);
 hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* E, int iters, uint64_t seed, int unit,

@@ -1,0 +1,234 @@
+// Monte-Carlo estimate of the two-stage sampler's distribution over the whole vocabulary
+// (FlashHead paper, Appendix D.1 "Monte-Carlo Simulation"): the average, over N probe sets
+// S_i drawn like the sampler's stage 1, of the full conditional p(v | h, S_i), the softmax of
+// z / tau over the tokens of S_i (zero elsewhere); entries no S_i reaches are optionally
+// clipped to the smallest non-zero estimate of the row.
+//
+// The conditional factors through per-cluster statistics.  With M_k = max_j z_kj / tau and
+// Zc_k = sum_j exp(z_kj / tau - M_k), the probe set S contributes to token (k, j), k in S,
+//   exp(z_kj / tau - M_k) * w_k(S),   w_k(S) = exp(M_k - m_S) / sum_{l in S} Zc_l exp(M_l - m_S),
+// m_S = max_{l in S} M_l.  So each probe set adds p weights into a per-cluster accumulator
+// A_k = sum_i [k in S_i] w_k(S_i) -- c values instead of a V-vector -- and one pass at the
+// end expands est(k, j) = exp(z_kj / tau - M_k) A_k / N into vocabulary order.
+//
+// Kernels, in stream order (the logits z and centroid logits s come from the forward path):
+//   k_mc_stats   one thread per (row, cluster): M_k, Zc_k; clears A_k and the row minimum;
+//   k_mc_sets    one 1024-thread workgroup per (probe set i, row): the stage-1 keys
+//                s / tau + G(seed, row, step = i, stream 0, k) (the sampler's own keys at
+//                step i), the exact top-p (select_regs), then w_k(S_i) added into A (fp64
+//                atomics: the order of the additions, and so the last bits, vary by run);
+//   k_mc_expand  one thread per (row, token slot): the estimate, scattered to out[row][C2T],
+//                and the row's smallest non-zero estimate;
+//   k_mc_clip    zeros replaced by that minimum (if clipping).
+// Softmax statistics, weights and estimates are fp64.
+#include <hip/hip_runtime.h>
+
+#include "fh_device.h"
+#include "fh_internal.h"
+#include "fh_select.h"
+
+namespace fh {
+namespace {
+
+constexpr int kMcThreads = 256;
+
+__global__ __launch_bounds__(kMcThreads) void k_mc_stats(const float* z, int B, int c, int b, double tau,
+                                                         double* M, double* Zc, double* A, uint64_t* minneg) {
+  const int64_t i = (int64_t)blockIdx.x * kMcThreads + threadIdx.x;     // row * c + cluster
+  if (i < (int64_t)B * c) {
+    const float* zk = z + i * b;
+    double m = -INFINITY;
+    for (int j = 0; j < b; ++j) m = fmax(m, (double)zk[j] / tau);
+    double s = 0.0;
+    for (int j = 0; j < b; ++j) s += exp((double)zk[j] / tau - m);
+    M[i] = m;
+    Zc[i] = s;
+    A[i] = 0.0;
+  }
+  if (i < B) minneg[i] = 0ull;
+}
+
+// Block-wide max / sum of one double per thread; every thread gets the result.  The order of
+// the additions is fixed (xor butterfly in each wave, then the waves in order).
+template <bool MAX>
+__device__ __forceinline__ double block_reduce_f64(double v, double* red) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const double y = __shfl_xor(v, o, kWave);
+    v = MAX ? fmax(v, y) : v + y;
+  }
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  double r = red[0];
+  for (int w = 1; w < nw; ++w) r = MAX ? fmax(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+struct McParams {
+  const float* s;        // [B][c] centroid logits
+  const double* M;       // [B][c]
+  const double* Zc;      // [B][c]
+  double* A;             // [B][c] accumulated weights
+  int c, p;
+  float tau;
+  uint64_t seed;
+  uint64_t set0;         // index of the first probe set of this launch
+};
+
+// Thread t holds the keys of clusters 4 (t + j NT) + e, j < KV, e < 4 (the four words of one
+// Philox block), as order-preserving uint32.
+template <int KV>
+__global__ __launch_bounds__(kSelThreads) void k_mc_sets(McParams a) {
+  __shared__ SelShared S;
+  __shared__ double red[kSelThreads / kWave];
+  const int r = blockIdx.y, tid = threadIdx.x, NT = blockDim.x, c = a.c;
+  const Rng g = make_rng(a.seed, a.set0 + blockIdx.x);
+  const float* s = a.s + (size_t)r * c;
+  uint32_t u[KV][4];
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int id0 = 4 * (tid + j * NT);
+    u[j][0] = u[j][1] = u[j][2] = u[j][3] = 0u;
+    if (id0 < c) {
+      const uint4 w = rng_block(g, (uint32_t)r, 0u, (uint32_t)id0 >> 2);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (id0 + e < c) u[j][e] = ord_key(sample_key(s[id0 + e], a.tau, ws[e]));
+    }
+  }
+  for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
+  for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
+  uint32_t Tu;
+  int Tid;
+  select_regs<KV>(u, c, a.p, S, Tu, Tid);
+  auto kept = [&](int j, int e) {
+    const int id = 4 * (tid + j * NT) + e;
+    return id < c && (u[j][e] > Tu || (u[j][e] == Tu && id <= Tid));
+  };
+  const double* Mr = a.M + (size_t)r * c;
+  const double* Zr = a.Zc + (size_t)r * c;
+  double* Ar = a.A + (size_t)r * c;
+  double mloc = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (kept(j, e)) mloc = fmax(mloc, Mr[4 * (tid + j * NT) + e]);
+  const double m = block_reduce_f64<true>(mloc, red);
+  double zl = 0.0;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (kept(j, e)) {
+        const int id = 4 * (tid + j * NT) + e;
+        zl += Zr[id] * exp(Mr[id] - m);
+      }
+  const double inv = 1.0 / block_reduce_f64<false>(zl, red);
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (kept(j, e)) {
+        const int id = 4 * (tid + j * NT) + e;
+        unsafeAtomicAdd(&Ar[id], exp(Mr[id] - m) * inv);
+      }
+}
+
+// grid (ceil(V / kMcThreads), B): a wave never spans two rows.
+__global__ __launch_bounds__(kMcThreads) void k_mc_expand(const float* z, const int32_t* c2t, const double* M,
+                                                          const double* A, int c, int b, int V, double tau,
+                                                          double inv_n, double* out, uint64_t* minneg) {
+  const int r = blockIdx.y;
+  const int slot = blockIdx.x * kMcThreads + threadIdx.x;           // k b + j
+  uint64_t key = 0ull;
+  if (slot < V) {
+    const int k = slot / b;
+    const size_t rk = (size_t)r * c + k;
+    const double Ak = A[rk];
+    double est = 0.0;
+    if (Ak > 0.0) est = exp((double)z[(size_t)r * V + slot] / tau - M[rk]) * Ak * inv_n;
+    out[(size_t)r * V + c2t[slot]] = est;
+    // positive doubles order like their bit patterns: the smallest has the largest complement
+    if (est > 0.0) key = ~(uint64_t)__double_as_longlong(est);
+  }
+  key = wave_max_u64(key);
+  if ((threadIdx.x & 63) == 0 && key) atomicMax((unsigned long long*)&minneg[r], (unsigned long long)key);
+}
+
+__global__ __launch_bounds__(kMcThreads) void k_mc_clip(int V, const uint64_t* minneg, double* out) {
+  const int r = blockIdx.y;
+  const int t = blockIdx.x * kMcThreads + threadIdx.x;
+  const uint64_t key = minneg[r];
+  if (t < V && key) {
+    double* o = out + (size_t)r * V + t;
+    if (*o == 0.0) *o = __longlong_as_double((long long)~key);
+  }
+}
+
+template <int KV>
+hipError_t launch_sets(const McParams& a, int B, int64_t n_sets, hipStream_t st) {
+  // probe sets in launches of at most 2^20 workgroups along x
+  McParams q = a;
+  for (int64_t i0 = 0; i0 < n_sets; i0 += (int64_t)1 << 20) {
+    const int64_t n = n_sets - i0 < ((int64_t)1 << 20) ? n_sets - i0 : ((int64_t)1 << 20);
+    q.set0 = a.set0 + (uint64_t)i0;
+    hipLaunchKernelGGL(k_mc_sets<KV>, dim3((unsigned)n, (unsigned)B), dim3(kSelThreads), 0, st, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+McWorkspace carve_mc_workspace(void* base, int B, int c, int b) {
+  const Workspace fw = carve_workspace(nullptr, B, c, c);
+  size_t off = (fw.bytes + 255) & ~(size_t)255;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = (off + n + 255) & ~(size_t)255;
+    return base ? (char*)base + o : nullptr;
+  };
+  McWorkspace w;
+  w.fw = carve_workspace(base, B, c, c);
+  w.s = (float*)take((size_t)B * c * sizeof(float));
+  w.z = (float*)take((size_t)B * c * b * sizeof(float));
+  w.M = (double*)take((size_t)B * c * sizeof(double));
+  w.Zc = (double*)take((size_t)B * c * sizeof(double));
+  w.A = (double*)take((size_t)B * c * sizeof(double));
+  w.minneg = (uint64_t*)take((size_t)B * sizeof(uint64_t));
+  w.token = (int32_t*)take((size_t)B * sizeof(int32_t));
+  w.bytes = off;
+  return w;
+}
+
+hipError_t launch_mc(const HeadShape& sh, int p, float tau, uint64_t seed, int64_t n_sets, int clip,
+                     const int32_t* c2t, const McWorkspace& w, double* out, hipStream_t st) {
+  const int B = sh.B, c = sh.c, b = sh.b, V = c * b;
+  const int64_t nk = (int64_t)B * c;
+  hipLaunchKernelGGL(k_mc_stats, dim3((unsigned)((nk + kMcThreads - 1) / kMcThreads)), dim3(kMcThreads), 0, st,
+                     w.z, B, c, b, (double)tau, w.M, w.Zc, w.A, w.minneg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  McParams a{w.s, w.M, w.Zc, w.A, c, p, tau, seed, 0};
+  if (c <= 4 * kSelThreads) e = launch_sets<1>(a, B, n_sets, st);
+  else if (c <= 8 * kSelThreads) e = launch_sets<2>(a, B, n_sets, st);
+  else if (c <= 16 * kSelThreads) e = launch_sets<4>(a, B, n_sets, st);
+  else e = launch_sets<8>(a, B, n_sets, st);
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)((V + kMcThreads - 1) / kMcThreads), (unsigned)B);
+  hipLaunchKernelGGL(k_mc_expand, g, dim3(kMcThreads), 0, st, w.z, c2t, w.M, w.A, c, b, V, (double)tau,
+                     1.0 / (double)n_sets, out, w.minneg);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (clip) {
+    hipLaunchKernelGGL(k_mc_clip, g, dim3(kMcThreads), 0, st, V, w.minneg, out);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace fh

@@ -73,6 +73,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_probe_logits": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
         "flashhead_select_and_probe": ([D, i64, vp, vp, vp, vp, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
         "flashhead_forward": ([D, vp, vp, vp, vp, vp, i64, i32, f32, u64, u64, vp, sz, O, vp], ctypes.c_int),
+        "flashhead_mc_marginal_workspace_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
+        "flashhead_mc_marginal": ([D, vp, vp, vp, vp, vp, i64, f32, u64, i64, i32, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_dense_workspace_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_dense_forward": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp, vp], ctypes.c_int),
     }
@@ -229,3 +231,17 @@ def flashhead_dense_forward(desc: fh_desc, h, E, mode, temperature, seed, step, 
         ctypes.byref(desc), _ptr(h), _ptr(E), _mode(mode), float(temperature), int(seed), int(step),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(token), _ptr(logits),
         _stream(stream)))
+
+
+def flashhead_mc_marginal_workspace_bytes(desc: fh_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().flashhead_mc_marginal_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def flashhead_mc_marginal(desc: fh_desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, temperature, seed,
+                          n_sets, clip, workspace, out, stream=None) -> None:
+    _check(load_library().flashhead_mc_marginal(
+        ctypes.byref(desc), _ptr(h), _ptr(centroids), _ptr(cluster_tokens), _ptr(E_tiles), _ptr(E_scales), int(p),
+        float(temperature), int(seed), int(n_sets), int(bool(clip)), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))

@@ -86,6 +86,19 @@ class DeviceHead:
                              ws, fo, stream=stream)
         return o
 
+    def mc_marginal(self, h: torch.Tensor, p: int, tau=1.0, seed=0, n_sets=10000, clip=True, out=None,
+                    stream=None, workspace=None) -> torch.Tensor:
+        """Monte-Carlo estimate of the sampler's distribution, float64 [B][V] by vocabulary id."""
+        B = h.shape[0]
+        desc = self.desc(B)
+        ws = workspace
+        if ws is None:
+            ws = torch.empty(fh.flashhead_mc_marginal_workspace_bytes(desc), dtype=torch.uint8, device=self.device)
+        o = out if out is not None else torch.empty(B, self.V, dtype=torch.float64, device=self.device)
+        fh.flashhead_mc_marginal(desc, h, self.C, self.c2t, self.tiles, self.scales, p, tau, seed, n_sets, clip, ws,
+                                 o, stream=stream)
+        return o
+
     def dense(self, h: torch.Tensor, mode="greedy", tau=1.0, seed=0, step=0, logits=False, stream=None,
               token=None, workspace=None) -> dict:
         assert self.E is not None, "constructed without keep_dense"

@@ -252,6 +252,33 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
                             uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
                             const fh_outputs* out, void* stream);
 
+/* Workspace size (bytes, device memory) for flashhead_mc_marginal. */
+fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* bytes);
+
+/*
+ * Monte-Carlo estimate of the two-stage sampler's distribution over the whole vocabulary
+ * (Appendix D.1, "Monte-Carlo Simulation"): for probe sets S_0 .. S_{N-1}, N = n_sets, drawn
+ * as the sampler's stage 1 draws them -- S_i is the Gumbel-top-p set of the keys
+ * s / tau + G(U(seed, r, step = i, 0, k)), i.e. flashhead_forward's probe set at step i --
+ *   out[r][v] = (1 / N) sum_i p(v | h_r, S_i),
+ * p(v | h, S) the softmax of z / tau over the tokens of the clusters in S (0 for the
+ * others).  With clip = 1 every zero entry of a row (a token no S_i reached) is replaced
+ * by the row's smallest non-zero entry, as the appendix does before taking logarithms.
+ *   h, centroids, cluster_tokens, E_tiles, E_scales, p   as for flashhead_forward
+ *   temperature    > 0, used by both stages
+ *   n_sets         1 <= n_sets < 2^31
+ *   clip           0 | 1
+ *   workspace      device, >= flashhead_mc_marginal_workspace_bytes(desc)
+ *   out            device double [B][V], indexed by vocabulary id
+ * The logits z and s are those of flashhead_forward (fp32 accumulation); the softmax
+ * statistics and the average are fp64, accumulated with atomic adds whose order varies
+ * between runs (the last bits of `out` may too).
+ */
+fh_status flashhead_mc_marginal(const fh_desc* desc, const void* h, const void* centroids,
+                                const int32_t* cluster_tokens, const void* E_tiles, const void* E_scales,
+                                int64_t p, float temperature, uint64_t seed, int64_t n_sets, int32_t clip,
+                                void* workspace, size_t workspace_bytes, double* out, void* stream);
+
 /* Workspace size (bytes) for flashhead_dense_forward. */
 fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes);
 

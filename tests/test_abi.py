@@ -137,3 +137,29 @@ def test_binding_raises(lib):
     with pytest.raises(fh.FlashHeadError) as ei:
         fh.flashhead_workspace_bytes(fh.make_desc(1, 1152, 262145, 16384), 4)
     assert ei.value.status == fh.FH_ERR_SHAPE
+
+
+def _mc(desc, p=8, tau=1.0, n_sets=100, clip=1, h=FAKE, C=FAKE, c2t=FAKE, tiles=FAKE, scales=None, ws=FAKE,
+        ws_bytes=1 << 34, out=FAKE):
+    return fh.load_library().flashhead_mc_marginal(ctypes.byref(desc), h, C, c2t, tiles, scales, p, tau, 0, n_sets,
+                                                   clip, ws, ws_bytes, out, None)
+
+
+def test_mc_marginal_argument_checks(lib):
+    d = fh.make_desc(1, 1152, 262144, 16384)
+    need = fh.flashhead_mc_marginal_workspace_bytes(d)
+    # the forward workspace at p = c, the logits of every token, and fp64 per-cluster state
+    assert need >= fh.flashhead_workspace_bytes(d, 16384) + 262144 * 4 + 3 * 16384 * 8
+    assert _mc(d, tau=0.0) == fh.FH_ERR_ARG
+    assert _mc(d, tau=float("inf")) == fh.FH_ERR_ARG
+    assert _mc(d, p=0) == fh.FH_ERR_ARG
+    assert _mc(d, p=16385) == fh.FH_ERR_ARG
+    assert _mc(d, n_sets=0) == fh.FH_ERR_ARG
+    assert _mc(d, n_sets=1 << 31) == fh.FH_ERR_ARG
+    assert _mc(d, clip=2) == fh.FH_ERR_ARG
+    assert _mc(d, out=None) == fh.FH_ERR_ARG
+    assert _mc(d, C=None) == fh.FH_ERR_ARG
+    assert _mc(d, ws=None) == fh.FH_ERR_WORKSPACE
+    assert _mc(d, ws_bytes=need - 1) == fh.FH_ERR_WORKSPACE
+    d4 = fh.make_desc(1, 3072, 128256, 8016, e_dtype="int4")
+    assert _mc(d4, scales=None) == fh.FH_ERR_ARG
