@@ -143,6 +143,8 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=0, help="copies of the head cycled through (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-head comparator")
+    ap.add_argument("--no-mc", action="store_true", help="skip the Monte-Carlo marginal (N = 10^4 probe sets)")
+    ap.add_argument("--mc-sets", type=int, default=10000, help="probe sets of the Monte-Carlo marginal")
     ap.add_argument("--copy-calib", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
 
@@ -272,6 +274,33 @@ def main() -> int:
             f"FlashHead speedup {t_d / t_call:.2f}x (byte ratio {dense_bytes / alg_bytes:.2f}x)")
         del g_d, E2
 
+    mc = None
+    if not args.no_mc:
+        # Appendix D.1's estimator: N probe sets per hidden state, the whole-vocabulary estimate
+        mws = torch.empty(fh.flashhead_mc_marginal_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        mout = torch.empty(B, wl.V, dtype=torch.float64, device="cuda")
+        n_mc = args.mc_sets
+
+        def mc_call(i):
+            fh.flashhead_mc_marginal(desc, Hs[i % R], Cs[i % R], dev.c2t, Ts[i % R], Ss[i % R], p, 1.0,
+                                     wl.sample_seed, n_mc, True, mws, mout)
+
+        mc_call(0)
+        torch.cuda.synchronize()
+        reps_mc = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps_mc):
+            mc_call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        t_mc = e0.elapsed_time(e1) / 1e3 / reps_mc
+        mc = {"n_sets": n_mc, "p": p, "tau": 1.0, "ms_per_call": round(t_mc * 1e3, 3),
+              "sets_per_s": round(B * n_mc / t_mc, 0), "us_per_set": round(t_mc * 1e6 / (B * n_mc), 4)}
+        log(f"Monte-Carlo marginal: {n_mc} probe sets in {t_mc * 1e3:.2f} ms "
+            f"({B * n_mc / t_mc:.3g} sets/s)")
+        del mws, mout
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b_ = torch.empty_like(a)
@@ -320,6 +349,7 @@ def main() -> int:
         "kernels": {k: {"bytes_per_launch": b_, "us_per_launch": round(t_ * 1e6, 3),
                         "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_, _) in units.items()},
         "dense": dense,
+        "mc_marginal": mc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

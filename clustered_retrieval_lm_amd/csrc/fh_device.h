@@ -88,8 +88,12 @@ __device__ __forceinline__ float gumbel(float u) { return -logf(-logf(u)); }
 // Probe or token key: the logit itself (greedy) or logit / tau + Gumbel noise (sampling).
 // Adding +0 turns a -0 key into +0 (round to nearest), so keys compare the same as floats
 // and as ord_key values.
+__device__ __forceinline__ float gumbel_key(float z_over_tau, uint32_t word) {
+  return z_over_tau + gumbel(word_to_uniform(word)) + 0.0f;
+}
+
 __device__ __forceinline__ float sample_key(float z, float tau, uint32_t word) {
-  return z / tau + gumbel(word_to_uniform(word)) + 0.0f;
+  return gumbel_key(z / tau, word);
 }
 
 __device__ __forceinline__ float make_key(float z, int sample, float tau, const Rng& g, uint32_t row,

@@ -59,11 +59,15 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
 hipError_t launch_centroids(int d, int c, int b, int src_bf16, int dst_bf16, int unit, const void* E,
                             const int32_t* c2t, void* out, hipStream_t st);
 // Monte-Carlo marginal (fh_mc.hip): the forward workspace for p = c, then the centroid
-// logits s, all token logits z (tile order), the per-cluster softmax statistics M and Zc,
+// logits s (and s / tau, prefilter thresholds), all token logits z (tile order), the per-cluster softmax statistics M and Zc,
 // the accumulated weights A, the per-row minimum cell and the forward's token output.
 struct McWorkspace {
   Workspace fw;
   float* s;           // [B][c]
+  float* stau;        // [B][c] s / tau
+  uint32_t* t0u;      // [B] prefilter thresholds
+  float* range;       // [B][2] key range
+  float* mu;          // [B][256] expected key counts above candidate thresholds
   float* z;           // [B][c][b]
   double* M;          // [B][c]
   double* Zc;         // [B][c]

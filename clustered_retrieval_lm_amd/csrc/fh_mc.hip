@@ -13,14 +13,24 @@
 //
 // Kernels, in stream order (the logits z and centroid logits s come from the forward path):
 //   k_mc_stats   one thread per (row, cluster): M_k, Zc_k; clears A_k and the row minimum;
+//   k_mc_prep, k_mc_grid, k_mc_pick   s / tau (fp32, the division the sampler's keys use)
+//                and a prefilter threshold t0 per row (below);
 //   k_mc_sets    one 1024-thread workgroup per (probe set i, row): the stage-1 keys
 //                s / tau + G(seed, row, step = i, stream 0, k) (the sampler's own keys at
-//                step i), the exact top-p (select_regs), then w_k(S_i) added into A (fp64
-//                atomics: the order of the additions, and so the last bits, vary by run);
+//                step i), the exact top-p, then one thread per kept cluster (ascending id)
+//                adds w_k(S_i) into A (fp64 atomics: the order of the additions, and so the
+//                last bits, vary by run);
 //   k_mc_expand  one thread per (row, token slot): the estimate, scattered to out[row][C2T],
 //                and the row's smallest non-zero estimate;
 //   k_mc_clip    zeros replaced by that minimum (if clipping).
 // Softmax statistics, weights and estimates are fp64.
+//
+// Prefilter.  The key of cluster k exceeds t with probability 1 - exp(-exp(s_k / tau - t)),
+// so the expected number of keys above t is known per row.  t0 is the largest of 256 evenly
+// spaced thresholds at which that expectation still reaches p + 8 sqrt(p) + 16 (a count below
+// p is then more than seven standard deviations away); a probe set histograms only its keys >= t0
+// (select_interval) instead of all c.  If fewer than p keys reach t0 -- a many-sigma event --
+// the set falls back to the full selection, so the result is exact either way.
 #include <hip/hip_runtime.h>
 
 #include "fh_device.h"
@@ -31,6 +41,10 @@ namespace fh {
 namespace {
 
 constexpr int kMcThreads = 256;
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
 
 __global__ __launch_bounds__(kMcThreads) void k_mc_stats(const float* z, int B, int c, int b, double tau,
                                                          double* M, double* Zc, double* A, uint64_t* minneg) {
@@ -46,6 +60,70 @@ __global__ __launch_bounds__(kMcThreads) void k_mc_stats(const float* z, int B, 
     A[i] = 0.0;
   }
   if (i < B) minneg[i] = 0ull;
+}
+
+constexpr int kGrid = 256;      // candidate thresholds evaluated per row
+
+// s / tau per cluster and the row's range [min - 3, max + 17] of possible keys (the Gumbel
+// draws lie in [-ln(24 ln 2), -ln(-ln(1 - 2^-24))] ~ [-2.82, 16.7]).
+__global__ __launch_bounds__(kSelThreads) void k_mc_prep(const float* s, int c, float tau, float* stau,
+                                                         float* range) {
+  __shared__ float rmin[kSelThreads / kWave], rmax[kSelThreads / kWave];
+  const int r = blockIdx.x, tid = threadIdx.x, NT = blockDim.x, nw = NT >> 6, wave = tid >> 6;
+  const float* sr = s + (size_t)r * c;
+  float* ar = stau + (size_t)r * c;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int k = tid; k < c; k += NT) {
+    const float a = sr[k] / tau;
+    ar[k] = a;
+    lo = fminf(lo, a);
+    hi = fmaxf(hi, a);
+  }
+  lo = wave_minmax_f32<false>(lo);
+  hi = wave_minmax_f32<true>(hi);
+  if ((tid & 63) == 0) { rmin[wave] = lo; rmax[wave] = hi; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < nw; ++w) { lo = fminf(lo, rmin[w]); hi = fmaxf(hi, rmax[w]); }
+    range[2 * r] = lo - 3.0f;
+    range[2 * r + 1] = hi + 17.0f;
+  }
+}
+
+__device__ __forceinline__ float grid_point(const float* range, int r, int j) {
+  const float lo = range[2 * r], hi = range[2 * r + 1];
+  return lo + (hi - lo) * ((float)j / (float)kGrid);
+}
+
+// grid (kGrid, B): the expected number of keys above candidate threshold j of row r.
+__global__ __launch_bounds__(kMcThreads) void k_mc_grid(const float* stau, int c, const float* range, float* mu) {
+  __shared__ float part[kMcThreads / kWave];
+  const int j = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const float t = grid_point(range, r, j);
+  const float* ar = stau + (size_t)r * c;
+  float m = 0.0f;
+  for (int k = tid; k < c; k += kMcThreads) m += -expm1f(-expf(ar[k] - t));
+  m = wave_sum(m);
+  if ((tid & 63) == 0) part[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) mu[(size_t)r * kGrid + j] = part[0] + part[1] + part[2] + part[3];
+}
+
+// One wave per row: the largest candidate threshold whose expectation reaches the target, as an
+// order-preserving key (0: no filtering -- the target is out of reach or the range is not finite).
+__global__ __launch_bounds__(kWave) void k_mc_pick(const float* range, const float* mu, int c, int p,
+                                                   uint32_t* t0u) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const float target = (float)p + 8.0f * sqrtf((float)p) + 16.0f;
+  int best = -1;
+  for (int j = lane; j < kGrid; j += kWave)
+    if (mu[(size_t)r * kGrid + j] >= target) best = j;
+  for (int o = 32; o >= 1; o >>= 1) best = max(best, __shfl_xor(best, o, kWave));
+  if (lane == 0) {
+    const float lo = range[2 * r], hi = range[2 * r + 1];
+    const bool ok = best >= 0 && target < (float)c && hi - lo < 1e30f;
+    t0u[r] = ok ? ord_key(grid_point(range, r, best)) : 0u;
+  }
 }
 
 // Block-wide max / sum of one double per thread; every thread gets the result.  The order of
@@ -67,7 +145,8 @@ __device__ __forceinline__ double block_reduce_f64(double v, double* red) {
 }
 
 struct McParams {
-  const float* s;        // [B][c] centroid logits
+  const float* stau;     // [B][c] centroid logits / tau
+  const uint32_t* t0u;   // [B] prefilter threshold (order-preserving; 0: none)
   const double* M;       // [B][c]
   const double* Zc;      // [B][c]
   double* A;             // [B][c] accumulated weights
@@ -78,15 +157,22 @@ struct McParams {
 };
 
 // Thread t holds the keys of clusters 4 (t + j NT) + e, j < KV, e < 4 (the four words of one
-// Philox block), as order-preserving uint32.
-template <int KV>
-__global__ __launch_bounds__(kSelThreads) void k_mc_sets(McParams a) {
+// Philox block), as order-preserving uint32.  512-thread workgroups at <= 128 registers let two
+// probe sets share a CU, so one set's selection overlaps the other's key generation; above
+// 16384 clusters the workgroup has 1024 threads.
+template <int KV, int NT_>
+__global__ __launch_bounds__(NT_, NT_ == 512 ? 4 : 1) void k_mc_sets(McParams a) {
   __shared__ SelShared S;
   __shared__ double red[kSelThreads / kWave];
-  const int r = blockIdx.y, tid = threadIdx.x, NT = blockDim.x, c = a.c;
+  __shared__ int cnt_w[kSelThreads / kWave];
+  __shared__ uint32_t max_w[kSelThreads / kWave];
+  const int r = blockIdx.y, tid = threadIdx.x, NT = blockDim.x, c = a.c, wave = tid >> 6, nw = NT >> 6;
   const Rng g = make_rng(a.seed, a.set0 + blockIdx.x);
-  const float* s = a.s + (size_t)r * c;
+  const float* sr = a.stau + (size_t)r * c;
+  const uint32_t t0 = a.t0u[r];
   uint32_t u[KV][4];
+  int cnt = 0;
+  uint32_t umax = 0u;
 #pragma unroll
   for (int j = 0; j < KV; ++j) {
     const int id0 = 4 * (tid + j * NT);
@@ -96,46 +182,55 @@ __global__ __launch_bounds__(kSelThreads) void k_mc_sets(McParams a) {
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (id0 + e < c) u[j][e] = ord_key(sample_key(s[id0 + e], a.tau, ws[e]));
+        if (id0 + e < c) {
+          const uint32_t x = ord_key(gumbel_key(sr[id0 + e], ws[e]));
+          u[j][e] = x;
+          cnt += x >= t0;
+          umax = max(umax, x);
+        }
     }
   }
   for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
   for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
+  cnt = wave_sum_i32(cnt);
+  umax = wave_minmax_u32<true>(umax);
+  if ((tid & 63) == 0) { cnt_w[wave] = cnt; max_w[wave] = umax; }
+  __syncthreads();
+  cnt = 0;
+  umax = 0u;
+  for (int w = 0; w < nw; ++w) { cnt += cnt_w[w]; umax = max(umax, max_w[w]); }
   uint32_t Tu;
   int Tid;
-  select_regs<KV>(u, c, a.p, S, Tu, Tid);
-  auto kept = [&](int j, int e) {
-    const int id = 4 * (tid + j * NT) + e;
-    return id < c && (u[j][e] > Tu || (u[j][e] == Tu && id <= Tid));
-  };
+  if (t0 != 0u && cnt >= a.p) select_interval<KV>(u, c, S, t0, umax, a.p, cnt, Tu, Tid);
+  else select_regs<KV>(u, c, a.p, S, Tu, Tid);
+  // the kept clusters in ascending id: thread q (q < p, strided) takes the q-th of them
+  mark_kept<KV>(u, c, Tu, Tid, S);
+  const int nwords = (c + 31) >> 5;
   const double* Mr = a.M + (size_t)r * c;
   const double* Zr = a.Zc + (size_t)r * c;
   double* Ar = a.A + (size_t)r * c;
-  double mloc = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (kept(j, e)) mloc = fmax(mloc, Mr[4 * (tid + j * NT) + e]);
+  int k0 = -1;
+  double M0 = -INFINITY, Z0 = 0.0;
+  if (tid < a.p) {
+    k0 = kept_at(S, nwords, tid);
+    M0 = Mr[k0];
+    Z0 = Zr[k0];
+  }
+  double mloc = M0;
+  for (int q = tid + NT; q < a.p; q += NT) mloc = fmax(mloc, Mr[kept_at(S, nwords, q)]);
   const double m = block_reduce_f64<true>(mloc, red);
-  double zl = 0.0;
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (kept(j, e)) {
-        const int id = 4 * (tid + j * NT) + e;
-        zl += Zr[id] * exp(Mr[id] - m);
-      }
+  const double e0 = k0 >= 0 ? exp(M0 - m) : 0.0;
+  double zl = Z0 * e0;
+  for (int q = tid + NT; q < a.p; q += NT) {
+    const int k = kept_at(S, nwords, q);
+    zl += Zr[k] * exp(Mr[k] - m);
+  }
   const double inv = 1.0 / block_reduce_f64<false>(zl, red);
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (kept(j, e)) {
-        const int id = 4 * (tid + j * NT) + e;
-        unsafeAtomicAdd(&Ar[id], exp(Mr[id] - m) * inv);
-      }
+  if (k0 >= 0) unsafeAtomicAdd(&Ar[k0], e0 * inv);
+  for (int q = tid + NT; q < a.p; q += NT) {
+    const int k = kept_at(S, nwords, q);
+    unsafeAtomicAdd(&Ar[k], exp(Mr[k] - m) * inv);
+  }
 }
 
 // grid (ceil(V / kMcThreads), B): a wave never spans two rows.
@@ -169,14 +264,14 @@ __global__ __launch_bounds__(kMcThreads) void k_mc_clip(int V, const uint64_t* m
   }
 }
 
-template <int KV>
+template <int KV, int NT_>
 hipError_t launch_sets(const McParams& a, int B, int64_t n_sets, hipStream_t st) {
   // probe sets in launches of at most 2^20 workgroups along x
   McParams q = a;
   for (int64_t i0 = 0; i0 < n_sets; i0 += (int64_t)1 << 20) {
     const int64_t n = n_sets - i0 < ((int64_t)1 << 20) ? n_sets - i0 : ((int64_t)1 << 20);
     q.set0 = a.set0 + (uint64_t)i0;
-    hipLaunchKernelGGL(k_mc_sets<KV>, dim3((unsigned)n, (unsigned)B), dim3(kSelThreads), 0, st, q);
+    hipLaunchKernelGGL((k_mc_sets<KV, NT_>), dim3((unsigned)n, (unsigned)B), dim3(NT_), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -196,6 +291,10 @@ McWorkspace carve_mc_workspace(void* base, int B, int c, int b) {
   McWorkspace w;
   w.fw = carve_workspace(base, B, c, c);
   w.s = (float*)take((size_t)B * c * sizeof(float));
+  w.stau = (float*)take((size_t)B * c * sizeof(float));
+  w.t0u = (uint32_t*)take((size_t)B * sizeof(uint32_t));
+  w.range = (float*)take((size_t)B * 2 * sizeof(float));
+  w.mu = (float*)take((size_t)B * kGrid * sizeof(float));
   w.z = (float*)take((size_t)B * c * b * sizeof(float));
   w.M = (double*)take((size_t)B * c * sizeof(double));
   w.Zc = (double*)take((size_t)B * c * sizeof(double));
@@ -214,11 +313,18 @@ hipError_t launch_mc(const HeadShape& sh, int p, float tau, uint64_t seed, int64
                      w.z, B, c, b, (double)tau, w.M, w.Zc, w.A, w.minneg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  McParams a{w.s, w.M, w.Zc, w.A, c, p, tau, seed, 0};
-  if (c <= 4 * kSelThreads) e = launch_sets<1>(a, B, n_sets, st);
-  else if (c <= 8 * kSelThreads) e = launch_sets<2>(a, B, n_sets, st);
-  else if (c <= 16 * kSelThreads) e = launch_sets<4>(a, B, n_sets, st);
-  else e = launch_sets<8>(a, B, n_sets, st);
+  hipLaunchKernelGGL(k_mc_prep, dim3((unsigned)B), dim3(kSelThreads), 0, st, w.s, c, tau, w.stau, w.range);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_mc_grid, dim3(kGrid, (unsigned)B), dim3(kMcThreads), 0, st, w.stau, c, w.range, w.mu);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_mc_pick, dim3((unsigned)B), dim3(kWave), 0, st, w.range, w.mu, c, p, w.t0u);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  McParams a{w.stau, w.t0u, w.M, w.Zc, w.A, c, p, tau, seed, 0};
+  if (c <= 4 * 512) e = launch_sets<1, 512>(a, B, n_sets, st);
+  else if (c <= 8 * 512) e = launch_sets<2, 512>(a, B, n_sets, st);
+  else if (c <= 16 * 512) e = launch_sets<4, 512>(a, B, n_sets, st);
+  else if (c <= 32 * 512) e = launch_sets<8, 512>(a, B, n_sets, st);
+  else e = launch_sets<8, 1024>(a, B, n_sets, st);
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((V + kMcThreads - 1) / kMcThreads), (unsigned)B);
   hipLaunchKernelGGL(k_mc_expand, g, dim3(kMcThreads), 0, st, w.z, c2t, w.M, w.A, c, b, V, (double)tau,

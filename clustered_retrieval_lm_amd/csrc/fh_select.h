@@ -43,7 +43,8 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
 // (larger key <=> larger u; ties go to the smaller id).  The result is the boundary
 // (Tu, Tid): a key is kept iff u > Tu, or u == Tu and id <= Tid.
 //
-// The candidate interval [ilo, ihi] (in u) starts as all keys.  A pass histograms the
+// The candidate interval [ilo, ihi] (in u) starts as all keys (select_regs) or as a range
+// known to hold the boundary (select_interval).  A pass histograms the
 // candidates into 2048 bins and shrinks the interval to the bin holding the boundary; bins
 // above it hold only larger keys and are kept.  The first two passes use bins linear in the
 // key's float value between the interval's ends (a monotone map that spreads the keys near
@@ -145,20 +146,14 @@ __device__ __forceinline__ void load_keys(const float* keys, int c, uint32_t (&u
   for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
 }
 
+// The selection restricted to the keys in [ilo, ihi] (order-preserving values): every key
+// above ihi is kept, and the `need` largest of the n_in keys in the interval complete the set
+// (n_in >= need).  Expects S.hist cleared (and a barrier since) and S.bitmap clear.
 template <int KV>
-__device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, int p, SelShared& S,
-                                            uint32_t& Tu, int& Tid) {
+__device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int c, SelShared& S, uint32_t ilo,
+                                                uint32_t ihi, int need, int n_in, uint32_t& Tu, int& Tid) {
   const int tid = threadIdx.x, NT = blockDim.x;
   auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
-  uint32_t vmax = 0u, vmin = 0xFFFFFFFFu;
-#pragma unroll
-  for (int j = 0; j < KV; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (idof(j, e) < c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
-  uint32_t ihi = block_minmax<true>(vmax, S.wred[0]);
-  uint32_t ilo = block_minmax<false>(vmin, S.wred[1]);
-  int need = p, n_in = c;
   for (int level = 0; level < 8 && n_in > kCand && n_in > need && ilo != ihi; ++level) {
     const float lo_f = ord_to_float(ilo), hi_f = ord_to_float(ihi);
     const float inv = (float)kSelBins / (hi_f - lo_f);
@@ -270,6 +265,22 @@ __device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, i
   __syncthreads();
   Tu = ilo;
   Tid = S.Tid;
+}
+
+template <int KV>
+__device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, int p, SelShared& S,
+                                            uint32_t& Tu, int& Tid) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
+  uint32_t vmax = 0u, vmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < KV; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (idof(j, e) < c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
+  const uint32_t ihi = block_minmax<true>(vmax, S.wred[0]);
+  const uint32_t ilo = block_minmax<false>(vmin, S.wred[1]);
+  select_interval<KV>(u, c, S, ilo, ihi, p, c, Tu, Tid);
 }
 
 // Mark the kept keys in the bitmap and turn its word popcounts into prefix offsets (woff).
