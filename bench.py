@@ -15,6 +15,7 @@ its own probe set's tiles (R different probe sets touch ~R x 19 MB of the 604 MB
 Prints one JSON line.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma] [--mode greedy]
+       python bench.py --sweep      (clusters x probes grid at the Llama-3.2-1B head shape)
 """
 from __future__ import annotations
 
@@ -133,6 +134,81 @@ def cpu_baseline(wl, hd, C2T, budget_s=15.0):
             "sample": f"{n} greedy oracle.head.forward calls (B=1, full workload shape) in {dt:.1f} s"}
 
 
+def run_sweep(args) -> int:
+    """The clusters / probes grid of the paper's Table 7 at the Llama-3.2-1B head shape
+    (d = 2048, V = 128256, bf16): c in {4008, 8016, 16032} (b = 32, 16, 8), p in {128, 256, 512},
+    greedy, B = 1, timed like the main bench (graph replay over R centroid copies and R hidden
+    states), with the dense head as the comparator.  Synthetic heads of the workloads recipe
+    whose latent partition serves as the balanced clustering (latency does not depend on
+    which balanced clustering is used).  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from clustered_retrieval_lm_amd import flashhead as fh
+    from clustered_retrieval_lm_amd.head import DeviceHead, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = fh.load_library()
+    import ctypes
+    d, V = 2048, 128256
+    rows, dense = [], None
+    for ci, c in enumerate((4008, 8016, 16032)):
+        b = V // c
+        R = 16
+        hd = workloads.make_small(d, V, c, R, seed=500 + ci, sigma_c=0.02, sigma_n=0.01, dtype="bf16")
+        C2T = np.lexsort((np.arange(V), hd.latent)).reshape(c, b).astype(np.int32)
+        dev = DeviceHead.from_clusters(d, V, c, C2T, hd.E, "bf16", "bf16", "bf16", "bf16", device="cuda",
+                                       keep_dense=dense is None)
+        Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
+        Hs = [to_device(hd.h[r:r + 1], "cuda") for r in range(R)]
+        desc = dev.desc(1)
+        for p in (128, 256, 512):
+            ws = dev.workspace(1, p)
+            out = dev.outputs(1, p, probes=False)
+            fo = fh.make_outputs(out["token"])
+
+            def fwd(i):
+                st = lib.flashhead_forward(ctypes.byref(desc), Hs[i % R].data_ptr(), Cs[i % R].data_ptr(),
+                                           dev.c2t.data_ptr(), dev.tiles.data_ptr(), None, p, 0, 1.0, 0, i,
+                                           ws.data_ptr(), ws.numel(), ctypes.byref(fo),
+                                           torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+            t, g = time_graph(torch, fwd, 8 * R, 20, warm_reps=2)
+            del g
+            alg = c * d * 2 + p * b * (2 * d + 4) + 2 * d
+            rows.append({"c": c, "b": b, "p": p, "us_per_call": round(t * 1e6, 2),
+                         "calls_per_s": round(1.0 / t, 1), "algorithmic_bytes": alg,
+                         "achieved_GBps": round(alg / t / 1e9, 1)})
+            log(f"c={c} b={b} p={p}: {t * 1e6:.2f} us/call, {alg / t / 1e9:.0f} GB/s")
+        if dense is None:
+            dws = torch.empty(fh.flashhead_dense_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+            dtok = torch.empty(1, dtype=torch.int32, device="cuda")
+            E2 = [dev.E, dev.E.clone()]
+
+            def dense_call(i):
+                st = lib.flashhead_dense_forward(ctypes.byref(desc), Hs[i % R].data_ptr(), E2[i % 2].data_ptr(), 0,
+                                                 1.0, 0, i, dws.data_ptr(), dws.numel(), dtok.data_ptr(), None,
+                                                 torch.cuda.current_stream().cuda_stream)
+                if st != 0:
+                    raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+            t_d, g = time_graph(torch, dense_call, 20, 10, warm_reps=1)
+            del g, E2
+            dense = {"us_per_call": round(t_d * 1e6, 2), "bytes": V * d * 2,
+                     "achieved_GBps": round(V * d * 2 / t_d / 1e9, 1)}
+            log(f"dense head: {t_d * 1e6:.2f} us/call")
+        del dev, Cs, Hs, hd
+        torch.cuda.empty_cache()
+    for r in rows:
+        r["speedup_vs_dense"] = round(dense["us_per_call"] / r["us_per_call"], 2)
+    print(json.dumps({"sweep": "clusters x probes (FlashHead Table 7 grid), Llama-3.2-1B head shape, bf16, "
+                               "B=1, greedy, synthetic", "dense": dense, "rows": rows}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +221,8 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-head comparator")
     ap.add_argument("--no-mc", action="store_true", help="skip the Monte-Carlo marginal (N = 10^4 probe sets)")
     ap.add_argument("--mc-sets", type=int, default=10000, help="probe sets of the Monte-Carlo marginal")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the clusters x probes grid (Table 7) at the Llama-3.2-1B head shape")
     ap.add_argument("--copy-calib", action="store_true", help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
 
@@ -153,6 +231,8 @@ def main() -> int:
         print(f"bench.py runs on one GPU only: the FlashHead head is measured on a single MI355X "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", flush=True)
         return 2
+    if args.sweep:
+        return run_sweep(args)
 
     import numpy as np
     import torch
