@@ -374,13 +374,20 @@ fh_status flashhead_mc_marginal(const fh_desc* desc, const void* h, const void* 
     return fail(FH_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes,
                 w.bytes);
   hipStream_t hs = (hipStream_t)stream;
-  // every logit of the head: the forward pass with p = c, greedy (its keys are the logits)
+  // every logit of the head: the centroid scores (greedy keys are the logits), then the token
+  // logits in tile order -- bf16 / fp32 tiles are a dense [V][d] matrix for the dense GEMV;
+  // int4 tiles go through the forward pass with p = c
   const fh::Sampling plain = sampling_of(FH_GREEDY, 1.0f, 0, 0);
   hipError_t e = fh::launch_scores(s, h, centroids, plain, w.fw, w.s, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
-  const fh_outputs all{w.token, nullptr, w.z, nullptr};
-  if ((st = select_and_probe(s, s.c, h, cluster_tokens, E_tiles, E_scales, plain, w.fw, &all, hs)) != FH_OK)
-    return st;
+  if (desc->e_dtype == FH_INT4_G128) {
+    const fh_outputs all{w.token, nullptr, w.z, nullptr};
+    if ((st = select_and_probe(s, s.c, h, cluster_tokens, E_tiles, E_scales, plain, w.fw, &all, hs)) != FH_OK)
+      return st;
+  } else {
+    e = fh::launch_dense(s, s.c * s.b, h, E_tiles, plain, w.fw.best, w.token, w.z, hs);
+    if (e != hipSuccess) return hip_fail(e, "tile logits launch");
+  }
   e = fh::launch_mc(s, (int)p, temperature, seed, n_sets, clip, cluster_tokens, w, out, hs);
   if (e != hipSuccess) return hip_fail(e, "Monte-Carlo marginal launch");
   return FH_OK;

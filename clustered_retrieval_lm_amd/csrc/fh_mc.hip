@@ -11,7 +11,8 @@
 // A_k = sum_i [k in S_i] w_k(S_i) -- c values instead of a V-vector -- and one pass at the
 // end expands est(k, j) = exp(z_kj / tau - M_k) A_k / N into vocabulary order.
 //
-// Kernels, in stream order (the logits z and centroid logits s come from the forward path):
+// Kernels, in stream order (the centroid logits s come from the stage-1 scores, the token
+// logits z, in tile order, from a dense pass over the tiles):
 //   k_mc_stats   one thread per (row, cluster): M_k, Zc_k; clears A_k and the row minimum;
 //   k_mc_prep, k_mc_grid, k_mc_pick   s / tau (fp32, the division the sampler's keys use)
 //                and a prefilter threshold t0 per row (below);

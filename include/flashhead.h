@@ -270,9 +270,11 @@ fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* byt
  *   clip           0 | 1
  *   workspace      device, >= flashhead_mc_marginal_workspace_bytes(desc)
  *   out            device double [B][V], indexed by vocabulary id
- * The logits z and s are those of flashhead_forward (fp32 accumulation); the softmax
- * statistics and the average are fp64, accumulated with atomic adds whose order varies
- * between runs (the last bits of `out` may too).
+ * The logits s and z are computed with fp32 accumulation (s as flashhead_centroid_scores;
+ * z over the whole tile array, as flashhead_dense_forward for bf16 / fp32 tiles and as
+ * flashhead_probe_logits for int4 tiles); the softmax statistics and the average are fp64,
+ * accumulated with atomic adds whose order varies between runs (the last bits of `out` may
+ * too).
  */
 fh_status flashhead_mc_marginal(const fh_desc* desc, const void* h, const void* centroids,
                                 const int32_t* cluster_tokens, const void* E_tiles, const void* E_scales,

@@ -149,7 +149,7 @@ def test_all_clusters_give_the_full_softmax(gpu):
     dev = DeviceHead(d, b * c, c, C, C2T, hd.E, "bf16", "bf16", "bf16", "bf16", device=gpu)
     raw, _ = _gpu_mc(dev, to_device(hd.h, gpu), c, tau, 3, 4)
     dr = ohead.dense_forward(hd.h, "bf16", hd.E, "bf16")
-    L2 = H.L_gemv("bf16", d)
+    L2 = max(H.L_gemv("bf16", d), H.L_mfma(d))
     for r in range(B):
         x = dr.z[r] / tau
         P = np.exp(x - x.max())
@@ -184,7 +184,9 @@ SMALL = [
     (136, 16, 1003, 3, 37, "bf16", "bf16", 0.7, 200),     # ragged c, B > 1 (Philox row = batch row)
     (96, 16, 300, 2, 20, "f32", "f32", 1.0, 250),
     (512, 16, 400, 2, 33, "bf16", "int4", 0.9, 200),      # int4 tiles
-    (64, 4, 5000, 1, 100, "bf16", "bf16", 1.2, 100),      # c > 4096: two key blocks per thread
+    (64, 4, 3000, 1, 60, "bf16", "bf16", 1.0, 100),       # 2048 < c <= 4096: two key blocks per thread
+    (64, 4, 5000, 1, 100, "bf16", "bf16", 1.2, 100),      # c <= 8192: four key blocks per thread
+    (64, 2, 20000, 1, 300, "bf16", "bf16", 1.0, 40),      # c > 16384: 1024-thread workgroups
 ]
 
 
@@ -200,7 +202,7 @@ def test_small_heads_match_the_oracle_estimator(gpu, d, b, c, B, p, dt, et, tau,
     tiles = ohead.pack_tiles(hd.E, dt, C2T, et)
     s, abss, z, absz = _oracle_logits(hd.h, dt, C, dt, C2T, tiles)
     L1 = H.L_stage1(B, dt, dt, d)
-    L2 = H.L_gemv(et, d)
+    L2 = max(H.L_gemv(et, d), H.L_mfma(d))     # z: dense GEMV, bf16 MFMA (B > 1) or int4 tiles
     for r in range(B):
         _check_row(raw[r], clip[r], s[r], abss[r], z[r], absz[r], C2T, p, tau, n_sets, seed, r, L1, L2,
                    max_flag=max(2, n_sets // 50))
