@@ -320,9 +320,6 @@ __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
   }
 }
 
-__device__ __forceinline__ int lane_prefix(uint64_t bal) {   // set bits of bal below this lane
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-}
 
 // Shared state of k_b1_stage2.  Keys live in registers: slot s of thread t holds the key of
 // cluster s * 1024 + t, so one wave ballot covers 64 consecutive clusters and the kept set

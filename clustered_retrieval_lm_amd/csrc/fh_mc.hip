@@ -157,6 +157,38 @@ struct McParams {
   uint64_t set0;         // index of the first probe set of this launch
 };
 
+// Probe-set weights shared by both probe-set kernels: S holds the kept bitmap with its prefix
+// offsets; thread q (q < p, strided) takes the q-th kept cluster in ascending id.
+__device__ __forceinline__ void add_set_weights(const McParams& a, int r, const SelShared& S, double* red) {
+  const int tid = threadIdx.x, NT = blockDim.x, c = a.c;
+  const int nwords = (c + 31) >> 5;
+  const double* Mr = a.M + (size_t)r * c;
+  const double* Zr = a.Zc + (size_t)r * c;
+  double* Ar = a.A + (size_t)r * c;
+  int k0 = -1;
+  double M0 = -INFINITY, Z0 = 0.0;
+  if (tid < a.p) {
+    k0 = kept_at(S, nwords, tid);
+    M0 = Mr[k0];
+    Z0 = Zr[k0];
+  }
+  double mloc = M0;
+  for (int q = tid + NT; q < a.p; q += NT) mloc = fmax(mloc, Mr[kept_at(S, nwords, q)]);
+  const double m = block_reduce_f64<true>(mloc, red);
+  const double e0 = k0 >= 0 ? exp(M0 - m) : 0.0;
+  double zl = Z0 * e0;
+  for (int q = tid + NT; q < a.p; q += NT) {
+    const int k = kept_at(S, nwords, q);
+    zl += Zr[k] * exp(Mr[k] - m);
+  }
+  const double inv = 1.0 / block_reduce_f64<false>(zl, red);
+  if (k0 >= 0) unsafeAtomicAdd(&Ar[k0], e0 * inv);
+  for (int q = tid + NT; q < a.p; q += NT) {
+    const int k = kept_at(S, nwords, q);
+    unsafeAtomicAdd(&Ar[k], exp(Mr[k] - m) * inv);
+  }
+}
+
 // Thread t holds the keys of clusters 4 (t + j NT) + e, j < KV, e < 4 (the four words of one
 // Philox block), as order-preserving uint32.  512-thread workgroups at <= 128 registers let two
 // probe sets share a CU, so one set's selection overlaps the other's key generation; above
@@ -204,34 +236,116 @@ __global__ __launch_bounds__(NT_, NT_ == 512 ? 4 : 1) void k_mc_sets(McParams a)
   int Tid;
   if (t0 != 0u && cnt >= a.p) select_interval<KV>(u, c, S, t0, umax, a.p, cnt, Tu, Tid);
   else select_regs<KV>(u, c, a.p, S, Tu, Tid);
-  // the kept clusters in ascending id: thread q (q < p, strided) takes the q-th of them
   mark_kept<KV>(u, c, Tu, Tid, S);
-  const int nwords = (c + 31) >> 5;
-  const double* Mr = a.M + (size_t)r * c;
-  const double* Zr = a.Zc + (size_t)r * c;
-  double* Ar = a.A + (size_t)r * c;
-  int k0 = -1;
-  double M0 = -INFINITY, Z0 = 0.0;
-  if (tid < a.p) {
-    k0 = kept_at(S, nwords, tid);
-    M0 = Mr[k0];
-    Z0 = Zr[k0];
+  add_set_weights(a, r, S, red);
+}
+
+constexpr int kListCap = 2048;     // candidate keys a probe set keeps in LDS
+constexpr int kListThreads = 512;
+
+// Keys recomputed from Philox on every call (the rare fallback of k_mc_sets_list).
+struct PhiloxKeys {
+  const float* sr;
+  Rng g;
+  uint32_t row;
+  int c;
+  template <class F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    for (int id4 = threadIdx.x; 4 * id4 < c; id4 += blockDim.x) {
+      const uint4 w = rng_block(g, row, 0u, (uint32_t)id4);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = 4 * id4 + e;
+        if (id < c) f(ord_key(gumbel_key(sr[id], ws[e])), id);
+      }
+    }
   }
-  double mloc = M0;
-  for (int q = tid + NT; q < a.p; q += NT) mloc = fmax(mloc, Mr[kept_at(S, nwords, q)]);
-  const double m = block_reduce_f64<true>(mloc, red);
-  const double e0 = k0 >= 0 ? exp(M0 - m) : 0.0;
-  double zl = Z0 * e0;
-  for (int q = tid + NT; q < a.p; q += NT) {
-    const int k = kept_at(S, nwords, q);
-    zl += Zr[k] * exp(Mr[k] - m);
+};
+
+// The candidate list in LDS.
+struct ListKeys {
+  const uint32_t* lu;
+  const int* lid;
+  int n;
+  template <class F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) f(lu[i], lid[i]);
   }
-  const double inv = 1.0 / block_reduce_f64<false>(zl, red);
-  if (k0 >= 0) unsafeAtomicAdd(&Ar[k0], e0 * inv);
-  for (int q = tid + NT; q < a.p; q += NT) {
-    const int k = kept_at(S, nwords, q);
-    unsafeAtomicAdd(&Ar[k], exp(Mr[k] - m) * inv);
+};
+
+// One probe set per workgroup, keys not held in registers: each key is computed once and, if
+// it reaches the row's threshold t0, appended to an LDS list (wave-aggregated slots); the
+// exact selection then runs over the list (keys below t0 cannot be kept when at least p keys
+// reach t0).  If the list holds fewer than p keys or overflows, or the row has no threshold,
+// the set recomputes its keys for every pass of the full selection instead.  Small register
+// and LDS footprints let four probe sets share a CU.
+__global__ __launch_bounds__(kListThreads, 8) void k_mc_sets_list(McParams a) {
+  __shared__ SelShared S;
+  __shared__ uint32_t lu[kListCap];
+  __shared__ int lid[kListCap];
+  __shared__ int nlist;
+  __shared__ uint32_t max_w[kListThreads / kWave], min_w[kListThreads / kWave];
+  __shared__ double red[kListThreads / kWave];
+  const int r = blockIdx.y, tid = threadIdx.x, NT = blockDim.x, c = a.c, lane = tid & 63, wave = tid >> 6;
+  const int nw = NT >> 6;
+  const Rng g = make_rng(a.seed, a.set0 + blockIdx.x);
+  const float* sr = a.stau + (size_t)r * c;
+  const uint32_t t0 = a.t0u[r];
+  if (tid == 0) nlist = 0;
+  for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
+  for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
+  __syncthreads();
+  uint32_t umax = 0u, umin = 0xFFFFFFFFu;
+  const int nblk = (c + 3) >> 2;
+  for (int b0 = 0; b0 < nblk; b0 += NT) {            // whole waves iterate together
+    const int id4 = b0 + tid;
+    uint32_t xs[4] = {0u, 0u, 0u, 0u};
+    if (id4 < nblk) {
+      const uint4 w = rng_block(g, (uint32_t)r, 0u, (uint32_t)id4);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * id4 + e < c) {
+          xs[e] = ord_key(gumbel_key(sr[4 * id4 + e], ws[e]));
+          umax = max(umax, xs[e]);
+          umin = min(umin, xs[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool take = id4 < nblk && 4 * id4 + e < c && t0 != 0u && xs[e] >= t0;
+      const uint64_t bal = __ballot(take);
+      if (bal) {
+        const int leader = __ffsll((unsigned long long)bal) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&nlist, __popcll(bal));
+        base = __shfl(base, leader, kWave);
+        if (take) {
+          const int slot = base + lane_prefix(bal);
+          if (slot < kListCap) { lu[slot] = xs[e]; lid[slot] = 4 * id4 + e; }
+        }
+      }
+    }
   }
+  umax = wave_minmax_u32<true>(umax);
+  umin = wave_minmax_u32<false>(umin);
+  if (lane == 0) { max_w[wave] = umax; min_w[wave] = umin; }
+  __syncthreads();
+  for (int w = 0; w < nw; ++w) { umax = max(umax, max_w[w]); umin = min(umin, min_w[w]); }
+  const int n = nlist;
+  uint32_t Tu;
+  int Tid;
+  if (t0 != 0u && n >= a.p && n <= kListCap) {
+    const ListKeys keys{lu, lid, n};
+    select_interval_each(keys, c, S, t0, umax, a.p, n, Tu, Tid);
+    mark_kept_each(keys, c, Tu, Tid, S);
+  } else {
+    const PhiloxKeys keys{sr, g, (uint32_t)r, c};
+    select_interval_each(keys, c, S, umin, umax, a.p, c, Tu, Tid);
+    mark_kept_each(keys, c, Tu, Tid, S);
+  }
+  add_set_weights(a, r, S, red);
 }
 
 // grid (ceil(V / kMcThreads), B): a wave never spans two rows.
@@ -265,14 +379,14 @@ __global__ __launch_bounds__(kMcThreads) void k_mc_clip(int V, const uint64_t* m
   }
 }
 
-template <int KV, int NT_>
-hipError_t launch_sets(const McParams& a, int B, int64_t n_sets, hipStream_t st) {
-  // probe sets in launches of at most 2^20 workgroups along x
+// Probe sets in launches of at most 2^20 workgroups along x.
+template <class K>
+hipError_t launch_sets(K kernel, int nt, const McParams& a, int B, int64_t n_sets, hipStream_t st) {
   McParams q = a;
   for (int64_t i0 = 0; i0 < n_sets; i0 += (int64_t)1 << 20) {
     const int64_t n = n_sets - i0 < ((int64_t)1 << 20) ? n_sets - i0 : ((int64_t)1 << 20);
     q.set0 = a.set0 + (uint64_t)i0;
-    hipLaunchKernelGGL((k_mc_sets<KV, NT_>), dim3((unsigned)n, (unsigned)B), dim3(NT_), 0, st, q);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)n, (unsigned)B), dim3(nt), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -321,11 +435,16 @@ hipError_t launch_mc(const HeadShape& sh, int p, float tau, uint64_t seed, int64
   hipLaunchKernelGGL(k_mc_pick, dim3((unsigned)B), dim3(kWave), 0, st, w.range, w.mu, c, p, w.t0u);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   McParams a{w.stau, w.t0u, w.M, w.Zc, w.A, c, p, tau, seed, 0};
-  if (c <= 4 * 512) e = launch_sets<1, 512>(a, B, n_sets, st);
-  else if (c <= 8 * 512) e = launch_sets<2, 512>(a, B, n_sets, st);
-  else if (c <= 16 * 512) e = launch_sets<4, 512>(a, B, n_sets, st);
-  else if (c <= 32 * 512) e = launch_sets<8, 512>(a, B, n_sets, st);
-  else e = launch_sets<8, 1024>(a, B, n_sets, st);
+  // the candidate-list kernel when the expected candidates (the target of k_mc_pick) fit its
+  // list with room to spare, else keys in registers
+  const float target = (float)p + 8.0f * sqrtf((float)p) + 16.0f;
+  if (target < (float)c && target <= 0.75f * (float)kListCap)
+    e = launch_sets(k_mc_sets_list, kListThreads, a, B, n_sets, st);
+  else if (c <= 4 * 512) e = launch_sets(k_mc_sets<1, 512>, 512, a, B, n_sets, st);
+  else if (c <= 8 * 512) e = launch_sets(k_mc_sets<2, 512>, 512, a, B, n_sets, st);
+  else if (c <= 16 * 512) e = launch_sets(k_mc_sets<4, 512>, 512, a, B, n_sets, st);
+  else if (c <= 32 * 512) e = launch_sets(k_mc_sets<8, 512>, 512, a, B, n_sets, st);
+  else e = launch_sets(k_mc_sets<8, 1024>, 1024, a, B, n_sets, st);
   if (e != hipSuccess) return e;
   const dim3 g((unsigned)((V + kMcThreads - 1) / kMcThreads), (unsigned)B);
   hipLaunchKernelGGL(k_mc_expand, g, dim3(kMcThreads), 0, st, w.z, c2t, w.M, w.A, c, b, V, (double)tau,

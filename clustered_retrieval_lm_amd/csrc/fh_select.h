@@ -148,12 +148,13 @@ __device__ __forceinline__ void load_keys(const float* keys, int c, uint32_t (&u
 
 // The selection restricted to the keys in [ilo, ihi] (order-preserving values): every key
 // above ihi is kept, and the `need` largest of the n_in keys in the interval complete the set
-// (n_in >= need).  Expects S.hist cleared (and a barrier since) and S.bitmap clear.
-template <int KV>
-__device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int c, SelShared& S, uint32_t ilo,
-                                                uint32_t ihi, int need, int n_in, uint32_t& Tu, int& Tid) {
+// (n_in >= need).  `each(f)` calls f(u, id) for every key this thread holds (id < c), in any
+// order; every call of `each` must present the same keys.  Expects S.hist cleared (and a
+// barrier since) and S.bitmap clear; leaves S.bitmap clear.
+template <class Each>
+__device__ __forceinline__ void select_interval_each(const Each& each, int c, SelShared& S, uint32_t ilo,
+                                                     uint32_t ihi, int need, int n_in, uint32_t& Tu, int& Tid) {
   const int tid = threadIdx.x, NT = blockDim.x;
-  auto idof = [&](int j, int e) { return 4 * (tid + j * NT) + e; };
   for (int level = 0; level < 8 && n_in > kCand && n_in > need && ilo != ihi; ++level) {
     const float lo_f = ord_to_float(ilo), hi_f = ord_to_float(ihi);
     const float inv = (float)kSelBins / (hi_f - lo_f);
@@ -163,12 +164,9 @@ __device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int 
       for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
       __syncthreads();
     }
-#pragma unroll
-    for (int j = 0; j < KV; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (idof(j, e) < c && u[j][e] >= ilo && u[j][e] <= ihi)
-          atomicAdd(&S.hist[sel_bin(u[j][e], flin, lo_f, inv, ilo, ushift)], 1);
+    each([&](uint32_t x, int) {
+      if (x >= ilo && x <= ihi) atomicAdd(&S.hist[sel_bin(x, flin, lo_f, inv, ilo, ushift)], 1);
+    });
     __syncthreads();
     // suffix counts from the top bin down: thread t owns bins 2047 - t*BPT - i
     const int bpt = kSelBins / NT;
@@ -190,16 +188,12 @@ __device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int 
     need -= S.bdig[1];
     n_in = S.bdig[2];
     uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < KV; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = u[j][e];
-        if (idof(j, e) < c && x >= ilo && x <= ihi && sel_bin(x, flin, lo_f, inv, ilo, ushift) == b) {
-          bmax = max(bmax, x);
-          bmin = min(bmin, x);
-        }
+    each([&](uint32_t x, int) {
+      if (x >= ilo && x <= ihi && sel_bin(x, flin, lo_f, inv, ilo, ushift) == b) {
+        bmax = max(bmax, x);
+        bmin = min(bmin, x);
       }
+    });
     ihi = block_minmax<true>(bmax, S.wred[2 + 2 * (level & 1)]);
     ilo = block_minmax<false>(bmin, S.wred[3 + 2 * (level & 1)]);
   }
@@ -212,14 +206,12 @@ __device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int 
   if (n_in <= kCand) {                        // rank the candidates exactly
     if (tid == 0) S.ncand = 0;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < KV; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (idof(j, e) < c && u[j][e] >= ilo && u[j][e] <= ihi) {
-          const int slot = atomicAdd(&S.ncand, 1);
-          if (slot < kCand) { S.cu[slot] = u[j][e]; S.cid[slot] = idof(j, e); }
-        }
+    each([&](uint32_t x, int id) {
+      if (x >= ilo && x <= ihi) {
+        const int slot = atomicAdd(&S.ncand, 1);
+        if (slot < kCand) { S.cu[slot] = x; S.cid[slot] = id; }
+      }
+    });
     __syncthreads();
     const int n = S.ncand < kCand ? S.ncand : kCand;
     for (int t = tid; t < n; t += NT) {
@@ -238,14 +230,9 @@ __device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int 
     return;
   }
   // many equal candidates (ilo == ihi): the need-th of them in id order, via the bitmap
-#pragma unroll
-  for (int j = 0; j < KV; ++j) {
-    uint32_t m = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) m |= (idof(j, e) < c && u[j][e] == ilo) ? (1u << e) : 0u;
-    const int id0 = idof(j, 0);
-    if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
-  }
+  each([&](uint32_t x, int id) {
+    if (x == ilo) atomicOr(&S.bitmap[id >> 5], 1u << (id & 31));
+  });
   __syncthreads();
   const int nwords = (c + 31) >> 5;
   for (int w0 = 0; w0 < nwords; w0 += NT) {
@@ -267,6 +254,30 @@ __device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int 
   Tid = S.Tid;
 }
 
+// Keys held in registers: thread t holds ids 4 (t + j NT) + e, j < KV, e < 4.
+template <int KV>
+struct RegKeys {
+  const uint32_t (&u)[KV][4];
+  int c;
+  template <class F>
+  __device__ __forceinline__ void operator()(F&& f) const {
+    const int tid = threadIdx.x, NT = blockDim.x;
+#pragma unroll
+    for (int j = 0; j < KV; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = 4 * (tid + j * NT) + e;
+        if (id < c) f(u[j][e], id);
+      }
+  }
+};
+
+template <int KV>
+__device__ __forceinline__ void select_interval(const uint32_t (&u)[KV][4], int c, SelShared& S, uint32_t ilo,
+                                                uint32_t ihi, int need, int n_in, uint32_t& Tu, int& Tid) {
+  select_interval_each(RegKeys<KV>{u, c}, c, S, ilo, ihi, need, n_in, Tu, Tid);
+}
+
 template <int KV>
 __device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, int p, SelShared& S,
                                             uint32_t& Tu, int& Tid) {
@@ -281,6 +292,22 @@ __device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, i
   const uint32_t ihi = block_minmax<true>(vmax, S.wred[0]);
   const uint32_t ilo = block_minmax<false>(vmin, S.wred[1]);
   select_interval<KV>(u, c, S, ilo, ihi, p, c, Tu, Tid);
+}
+
+// Word popcounts of S.bitmap turned into prefix offsets (S.woff), for kept_at.
+__device__ __forceinline__ void bitmap_prefix(int c, SelShared& S) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  const int nwords = (c + 31) >> 5;
+  int carry = 0;
+  for (int w0 = 0; w0 < nwords; w0 += NT) {
+    const int w = w0 + tid;
+    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
+    int tot;
+    const int before = block_scan(pc, S.wtot[4 + ((w0 / NT) & 1)], tot);
+    if (w < nwords) S.woff[w] = carry + before;
+    carry += tot;
+  }
+  __syncthreads();
 }
 
 // Mark the kept keys in the bitmap and turn its word popcounts into prefix offsets (woff).
@@ -299,17 +326,17 @@ __device__ __forceinline__ void mark_kept(const uint32_t (&u)[KV][4], int c, uin
     if (m) atomicOr(&S.bitmap[id0 >> 5], m << (id0 & 31));
   }
   __syncthreads();
-  const int nwords = (c + 31) >> 5;
-  int carry = 0;
-  for (int w0 = 0; w0 < nwords; w0 += NT) {
-    const int w = w0 + tid;
-    const int pc = w < nwords ? __popc(S.bitmap[w]) : 0;
-    int tot;
-    const int before = block_scan(pc, S.wtot[4 + ((w0 / NT) & 1)], tot);
-    if (w < nwords) S.woff[w] = carry + before;
-    carry += tot;
-  }
+  bitmap_prefix(c, S);
+}
+
+// The same for keys presented by `each` (as select_interval_each).
+template <class Each>
+__device__ __forceinline__ void mark_kept_each(const Each& each, int c, uint32_t Tu, int Tid, SelShared& S) {
+  each([&](uint32_t x, int id) {
+    if (x > Tu || (x == Tu && id <= Tid)) atomicOr(&S.bitmap[id >> 5], 1u << (id & 31));
+  });
   __syncthreads();
+  bitmap_prefix(c, S);
 }
 
 // Cluster id of ascending rank q among the kept ones (binary search over the word offsets).

@@ -186,7 +186,11 @@ SMALL = [
     (512, 16, 400, 2, 33, "bf16", "int4", 0.9, 200),      # int4 tiles
     (64, 4, 3000, 1, 60, "bf16", "bf16", 1.0, 100),       # 2048 < c <= 4096: two key blocks per thread
     (64, 4, 5000, 1, 100, "bf16", "bf16", 1.2, 100),      # c <= 8192: four key blocks per thread
-    (64, 2, 20000, 1, 300, "bf16", "bf16", 1.0, 40),      # c > 16384: 1024-thread workgroups
+    (64, 2, 20000, 1, 300, "bf16", "bf16", 1.0, 40),      # c > 16384
+    # p large enough that the candidates would not fit the LDS list: keys in registers
+    (64, 4, 3000, 1, 1400, "bf16", "bf16", 1.0, 30),      # two key blocks per thread
+    (64, 4, 5000, 1, 1500, "bf16", "bf16", 1.0, 30),      # four key blocks per thread
+    (64, 2, 20000, 1, 1300, "bf16", "bf16", 1.0, 20),     # c > 16384: 1024-thread workgroups
 ]
 
 
@@ -206,6 +210,32 @@ def test_small_heads_match_the_oracle_estimator(gpu, d, b, c, B, p, dt, et, tau,
     for r in range(B):
         _check_row(raw[r], clip[r], s[r], abss[r], z[r], absz[r], C2T, p, tau, n_sets, seed, r, L1, L2,
                    max_flag=max(2, n_sets // 50))
+
+
+def test_outlier_centroid_forces_the_full_selection(gpu):
+    """One centroid logit far above the rest stretches the key range the threshold grid spans,
+    so the chosen threshold lets far more than the LDS list holds through: every probe set
+    then runs the full selection on recomputed keys, and must still match the oracle."""
+    d, b, c, p, tau, seed, n_sets = 16, 2, 20000, 100, 1.0, 3, 12
+    rng = np.random.default_rng(99)
+    h = np.zeros((1, d), dtype=np.float32)
+    h[0, 0] = 1.0                                   # s_k = C[k][0] exactly
+    C = (rng.standard_normal((c, d)) * 0.01).astype(np.float32)
+    C[0, 0] = 1590.0                                # outlier: grid spacing ~6.3 key units
+    C[1, 0] = -2.5                                  # lowest grid point -5.5, next 0.83
+    E = (rng.standard_normal((c * b, d)) * 0.8).astype(np.float32)
+    C2T = np.sort(rng.permutation(c * b).reshape(c, b), axis=1).astype(np.int32)
+    s64 = C.astype(np.float64) @ h[0].astype(np.float64)
+    ks = np.arange(c)
+    above = [int(np.sum(s64 / tau + philox.gumbel(philox.uniform(seed, 0, i, 0, ks)) >= 0.83))
+             for i in range(n_sets)]
+    assert min(above) > 2048                        # the premise: the list would overflow
+    dev = DeviceHead(d, c * b, c, C, C2T, E, "f32", "f32", "f32", "f32", device=gpu)
+    raw, clip = _gpu_mc(dev, to_device(h, gpu), p, tau, seed, n_sets)
+    tiles = ohead.pack_tiles(E, "f32", C2T, "f32")
+    s, abss, z, absz = _oracle_logits(h, "f32", C, "f32", C2T, tiles)
+    _check_row(raw[0], clip[0], s[0], abss[0], z[0], absz[0], C2T, p, tau, n_sets, seed, 0,
+               H.L_gemv("f32", d), H.L_gemv("f32", d), max_flag=1)
 
 
 def test_gemma_shape_matches_the_oracle_estimator(gpu):
