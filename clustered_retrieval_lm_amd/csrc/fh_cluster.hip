@@ -29,6 +29,7 @@ constexpr int kTopM = 16;                  // most similar clusters kept per evi
 constexpr int kTile = 64;                  // similarity GEMM tile: tokens x clusters
 constexpr int kKc = 16;                    // GEMM depth per LDS stage
 constexpr int kMaxC = 32768;
+constexpr int kRescanWG = 1024;            // workgroups of k_km_rescan
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -53,7 +54,8 @@ __device__ __forceinline__ double load_e(const void* E, int src_bf16, size_t i) 
 }
 
 // En[i] = E[i] / ||E[i]|| (a zero row stays zero); one wave per row.
-__global__ __launch_bounds__(kKmThreads) void k_km_normalize(const void* E, int src_bf16, int V, int d, double* En) {
+__global__ __launch_bounds__(kKmThreads) void k_km_normalize(const void* E, int src_bf16, int V, int d, double* En,
+                                                              double* nrm) {
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * (kKmThreads / 64) + (threadIdx.x >> 6);
   if (i >= V) return;
@@ -63,6 +65,7 @@ __global__ __launch_bounds__(kKmThreads) void k_km_normalize(const void* E, int 
     ss = fma(x, x, ss);
   }
   const double n = sqrt(wave_sum_f64(ss));
+  if (lane == 0) nrm[i] = n;
   for (int j = lane; j < d; j += 64) {
     const double x = load_e(E, src_bf16, (size_t)i * d + j);
     En[(size_t)i * d + j] = n > 0.0 ? x / n : 0.0;
@@ -71,18 +74,45 @@ __global__ __launch_bounds__(kKmThreads) void k_km_normalize(const void* E, int 
 
 // k-means++ weights after draw m: w = max(2 - 2 e_i . e_new, 0) (m = 0) or the min of that
 // and w (m > 0); the new centre's weight is 0.  One wave per token.
-__global__ __launch_bounds__(kKmThreads) void k_km_weights(const double* En, int V, int d, const int32_t* chosen,
-                                                          int m, double* w) {
+// D^2 weights of k-means++ after centre m: w_i = min(w_i, max(2 - 2 cos(e_i, e_new), 0)) (w_i
+// itself for m = 0), 0 for the centre.  The cosine is the fp64 dot of the source rows (bf16 /
+// fp32 values, exact products) over the product of their norms -- the same quantity as the dot
+// of the normalised rows, from a quarter (bf16) or half (fp32) of their bytes.  One wave per
+// token, 16-byte loads.
+// Thread 0 also marks centre m used and primes chosen[m + 1] for the next draw's minimum.
+template <int SRC_BF16>
+__global__ __launch_bounds__(kKmThreads) void k_km_weights(const void* E, const double* nrm, int V, int d,
+                                                          int32_t* chosen, int m, int c, double* w, uint8_t* used) {
+  constexpr int EPC = SRC_BF16 ? 8 : 4;                // elements per 16-byte chunk
   const int lane = threadIdx.x & 63;
   const int i = blockIdx.x * (kKmThreads / 64) + (threadIdx.x >> 6);
   if (i >= V) return;
   const int nw = chosen[m];
-  const double* x = En + (size_t)i * d;
-  const double* y = En + (size_t)nw * d;
+  if (i == 0 && lane == 0) {
+    used[nw] = 1;
+    if (m + 1 < c) chosen[m + 1] = 0x7FFFFFFF;
+  }
+  const int nch = d / EPC;
+  const uint4* x = reinterpret_cast<const uint4*>((const char*)E + (size_t)i * d * (SRC_BF16 ? 2 : 4));
+  const uint4* y = reinterpret_cast<const uint4*>((const char*)E + (size_t)nw * d * (SRC_BF16 ? 2 : 4));
   double s = 0.0;
-  for (int j = lane; j < d; j += 64) s = fma(x[j], y[j], s);
-  const double dot = wave_sum_f64(s);
+  for (int q = lane; q < nch; q += 64) {
+    const uint4 a = x[q], b = y[q];
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (SRC_BF16) {
+        s = fma((double)__uint_as_float(av[k] << 16), (double)__uint_as_float(bv[k] << 16), s);
+        s = fma((double)__uint_as_float(av[k] & 0xFFFF0000u), (double)__uint_as_float(bv[k] & 0xFFFF0000u), s);
+      } else {
+        s = fma((double)__uint_as_float(av[k]), (double)__uint_as_float(bv[k]), s);
+      }
+    }
+  }
+  s = wave_sum_f64(s);
   if (lane == 0) {
+    const double ni = nrm[i], nn = nrm[nw];
+    const double dot = ni > 0.0 && nn > 0.0 ? s / (ni * nn) : 0.0;
     const double v = fmax(2.0 - 2.0 * dot, 0.0);
     double r = m == 0 ? v : fmin(w[i], v);
     if (i == nw) r = 0.0;
@@ -99,46 +129,20 @@ __global__ void k_km_first(int V, int first, int32_t* chosen, uint8_t* used) {
 // Draw m: the first i with cum(w)_i >= u * total; when every weight is 0, the smallest id
 // not chosen yet.  One workgroup: contiguous segments summed in order, then a sequential
 // scan of the segment sums.
-__global__ __launch_bounds__(1024) void k_km_draw(const double* w, int V, double u, int32_t* chosen, int m,
-                                                   uint8_t* used) {
-  __shared__ double pre[1024];
-  __shared__ double total;
-  __shared__ int best;
-  const int t = threadIdx.x;
-  const int per = (V + 1023) / 1024;
-  const int lo = min(V, t * per), hi = min(V, lo + per);
-  double s = 0.0;
-  for (int i = lo; i < hi; ++i) s += w[i];
-  pre[t] = s;
-  if (t == 0) best = 0x7FFFFFFF;
-  __syncthreads();
-  if (t == 0) {
-    double acc = 0.0;
-    for (int k = 0; k < 1024; ++k) {
-      const double v = pre[k];
-      pre[k] = acc;
-      acc += v;
-    }
-    total = acc;
-  }
-  __syncthreads();
-  const double tot = total;
+// The m-th draw by inverse CDF: the first token whose inclusive prefix sum of the weights
+// (`cum`, ascending id) reaches u times the total (atomic minimum into chosen[m], which the
+// previous k_km_weights set to INT_MAX); with a zero total, the smallest unused id.
+__global__ __launch_bounds__(kKmThreads) void k_km_draw(const double* cum, int V, double u, int32_t* chosen, int m,
+                                                        const uint8_t* used) {
+  const int i = blockIdx.x * kKmThreads + threadIdx.x;
+  if (i >= V) return;
+  const double tot = cum[V - 1];
   if (tot > 0.0) {
-    const double target = u * tot;
-    double acc = pre[t];
-    for (int i = lo; i < hi; ++i) {
-      acc += w[i];
-      if (acc >= target) { atomicMin(&best, i); break; }
-    }
-  } else {
-    for (int i = lo; i < hi; ++i)
-      if (!used[i]) { atomicMin(&best, i); break; }
-  }
-  __syncthreads();
-  if (t == 0) {
-    const int i = best < V ? best : V - 1;
-    chosen[m] = i;
-    used[i] = 1;
+    if (cum[i] >= u * tot) atomicMin(&chosen[m], i);
+  } else if (i == 0) {                             // every token coincides with a centre (degenerate)
+    int j = 0;
+    while (j < V - 1 && used[j]) ++j;
+    chosen[m] = j;
   }
 }
 
@@ -303,46 +307,86 @@ __global__ __launch_bounds__(kKmThreads) void k_km_topm(const double* En, const 
   }
 }
 
-// Evicted tokens in ascending id, each to its most similar cluster with room: the first
-// of its kTopM candidates with room, else a scan of every cluster.  One wave, in order.
-__global__ __launch_bounds__(64) void k_km_repair(const double* En, const double* Cn, const int32_t* ev, int n_ev,
-                                                   const int32_t* top, const int32_t* room_in, int c, int d,
-                                                   int32_t* a) {
+// Evicted tokens in ascending id, each to its most similar cluster with room: the first of
+// its kTopM candidates with room.  One wave walks the tokens from `pos` in order; at a token
+// whose candidates are all full it stops (*status = that position; n_ev when every token is
+// placed), and the host has k_km_rescan + k_km_place settle that token against every
+// cluster before the walk resumes.  `room` (global) carries the free slots between launches.
+__global__ __launch_bounds__(64) void k_km_repair(const int32_t* ev, int n_ev, int pos, const int32_t* top,
+                                                   int32_t* room_g, int c, int32_t* a, int32_t* status) {
   __shared__ uint16_t room[kMaxC];
   const int lane = threadIdx.x;
-  for (int k = lane; k < c; k += 64) room[k] = (uint16_t)room_in[k];
+  for (int k = lane; k < c; k += 64) room[k] = (uint16_t)room_g[k];
   __syncthreads();
-  for (int e = 0; e < n_ev; ++e) {
-    const int tok = ev[e];
-    int k = -1;
-    for (int q = 0; q < kTopM; ++q) {
-      const int kk = top[(size_t)e * kTopM + q];
-      if (kk >= 0 && room[kk] > 0) { k = kk; break; }
-    }
-    if (k < 0) {
-      const double* x = En + (size_t)tok * d;
-      double v = -INFINITY;
-      int kb = 0x7FFFFFFF;
-      for (int kk = lane; kk < c; kk += 64) {
-        if (room[kk] == 0) continue;
-        const double* y = Cn + (size_t)kk * d;
-        double s = 0.0;
-        for (int j = 0; j < d; ++j) s = fma(x[j], y[j], s);
-        if (sim_before(s, kk, v, kb)) { v = s; kb = kk; }
-      }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const double ov = __shfl_xor(v, m, kWave);
-        const int ok = __shfl_xor(kb, m, kWave);
-        if (sim_before(ov, ok, v, kb)) { v = ov; kb = ok; }
-      }
-      k = kb;
-    }
-    if (lane == 0 && k >= 0 && k < c) {      // total room equals the evicted count: always found
-      a[tok] = k;
+  int stop = n_ev;
+  for (int e = pos; e < n_ev; ++e) {
+    // lane q < kTopM looks at candidate q; the first with room wins
+    const int kk = lane < kTopM ? top[(size_t)e * kTopM + lane] : -1;
+    const bool ok = kk >= 0 && room[kk] > 0;
+    const uint64_t bal = __ballot(ok);
+    if (!bal) { stop = e; break; }
+    const int q = __ffsll((unsigned long long)bal) - 1;
+    const int k = __shfl(kk, q, kWave);
+    if (lane == 0) {
+      a[ev[e]] = k;
       room[k] = (uint16_t)(room[k] - 1);
     }
     __syncthreads();
+  }
+  __syncthreads();
+  for (int k = lane; k < c; k += 64) room_g[k] = room[k];
+  if (lane == 0) *status = stop;
+}
+
+// Token ev[pos] against every cluster with room: one wave per cluster (coalesced row dot),
+// the best (similarity desc, id asc) of each workgroup to part_v / part_k.
+__global__ __launch_bounds__(kKmThreads) void k_km_rescan(const double* En, const double* Cn, const int32_t* ev,
+                                                          const int32_t* status, const int32_t* room, int c, int d,
+                                                          double* part_v, int32_t* part_k) {
+  __shared__ double wv[kKmThreads / 64];
+  __shared__ int wk[kKmThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const double* x = En + (size_t)ev[*status] * d;
+  double v = -INFINITY;
+  int kb = 0x7FFFFFFF;
+  const int nwaves = gridDim.x * (kKmThreads / 64);
+  for (int k = blockIdx.x * (kKmThreads / 64) + wave; k < c; k += nwaves) {
+    if (room[k] <= 0) continue;                       // wave-uniform
+    const double* y = Cn + (size_t)k * d;
+    double s = 0.0;
+    for (int j = lane; j < d; j += 64) s = fma(x[j], y[j], s);
+    s = wave_sum_f64(s);
+    if (sim_before(s, k, v, kb)) { v = s; kb = k; }
+  }
+  if (lane == 0) { wv[wave] = v; wk[wave] = kb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kKmThreads / 64; ++w)
+      if (sim_before(wv[w], wk[w], v, kb)) { v = wv[w]; kb = wk[w]; }
+    part_v[blockIdx.x] = v;
+    part_k[blockIdx.x] = kb;
+  }
+}
+
+// The rescan's winner: token ev[pos] takes it (total room equals the evicted count, so a
+// cluster with room exists).
+__global__ __launch_bounds__(64) void k_km_place(const double* part_v, const int32_t* part_k, int g,
+                                                  const int32_t* ev, const int32_t* status, int c, int32_t* room,
+                                                  int32_t* a) {
+  const int lane = threadIdx.x;
+  double v = -INFINITY;
+  int kb = 0x7FFFFFFF;
+  for (int i = lane; i < g; i += 64)
+    if (sim_before(part_v[i], part_k[i], v, kb)) { v = part_v[i]; kb = part_k[i]; }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const double ov = __shfl_xor(v, m, kWave);
+    const int ok = __shfl_xor(kb, m, kWave);
+    if (sim_before(ov, ok, v, kb)) { v = ov; kb = ok; }
+  }
+  if (lane == 0 && kb >= 0 && kb < c) {
+    a[ev[*status]] = kb;
+    room[kb] -= 1;
   }
 }
 
@@ -391,8 +435,9 @@ __global__ void k_km_store_unit(const double* Cn, size_t n, int dst_bf16, void* 
 }
 
 struct KmWs {
-  double *En, *Cn, *w, *sbest;
-  int32_t *a, *chosen, *ids, *ids2, *key32, *key32b, *counts, *start, *room, *ev, *n_ev, *top;
+  double *En, *Cn, *w, *sbest, *nrm;
+  int32_t *a, *chosen, *ids, *ids2, *key32, *key32b, *counts, *start, *room, *ev, *n_ev, *top, *status, *part_k;
+  double* part_v;
   uint64_t *key64, *key64b;
   uint8_t *used, *flags;
   void* tmp;
@@ -409,7 +454,9 @@ size_t cub_tmp_bytes(int V, int c) {
   (void)hipcub::DeviceScan::ExclusiveSum(nullptr, s3, (const int32_t*)nullptr, (int32_t*)nullptr, c);
   (void)hipcub::DeviceSelect::Flagged(nullptr, s4, hipcub::CountingInputIterator<int32_t>(0),
                                       (const uint8_t*)nullptr, (int32_t*)nullptr, (int32_t*)nullptr, V);
-  return std::max(std::max(s1, s2), std::max(s3, s4));
+  size_t s5 = 0;
+  (void)hipcub::DeviceScan::InclusiveSum(nullptr, s5, (const double*)nullptr, (double*)nullptr, V);
+  return std::max(std::max(std::max(s1, s2), std::max(s3, s4)), s5);
 }
 
 KmWs km_carve(void* base, int V, int d, int c) {
@@ -426,6 +473,7 @@ KmWs km_carve(void* base, int V, int d, int c) {
   w.Cn = (double*)take((size_t)c * d * 8);
   w.w = (double*)take((size_t)V * 8);
   w.sbest = (double*)take((size_t)V * 8);
+  w.nrm = (double*)take((size_t)V * 8);
   w.a = (int32_t*)take((size_t)V * 4);
   w.chosen = (int32_t*)take((size_t)c * 4);
   w.ids = (int32_t*)take((size_t)V * 4);
@@ -437,6 +485,9 @@ KmWs km_carve(void* base, int V, int d, int c) {
   w.room = (int32_t*)take((size_t)c * 4);
   w.ev = (int32_t*)take((size_t)V * 4);
   w.n_ev = (int32_t*)take(4);
+  w.status = (int32_t*)take(4);
+  w.part_v = (double*)take((size_t)kRescanWG * 8);
+  w.part_k = (int32_t*)take((size_t)kRescanWG * 4);
   w.top = (int32_t*)take((size_t)V * kTopM * 4);
   w.key64 = (uint64_t*)take((size_t)V * 8);
   w.key64b = (uint64_t*)take((size_t)V * 8);
@@ -465,7 +516,8 @@ hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* 
     e = hipGetLastError();                      \
     if (e != hipSuccess) return e;              \
   } while (0)
-  hipLaunchKernelGGL(k_km_normalize, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, E, src_bf16, V, d, w.En);
+  hipLaunchKernelGGL(k_km_normalize, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, E, src_bf16, V, d, w.En,
+                     w.nrm);
   KM_CHECK();
   // ---- k-means++ (Philox stream 2, row 0, step m, element 0)
   auto uni = [&](int m) {
@@ -476,13 +528,22 @@ hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* 
   int first = (int)floor(u0 * V);
   if (first > V - 1) first = V - 1;
   hipLaunchKernelGGL(k_km_first, dim3(blocks(V, 256)), dim3(256), 0, st, V, first, w.chosen, w.used);
-  hipLaunchKernelGGL(k_km_weights, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, (const double*)w.En, V, d,
-                     (const int32_t*)w.chosen, 0, w.w);
+  auto weights = [&](int m) {
+    if (src_bf16)
+      hipLaunchKernelGGL(k_km_weights<1>, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, E, (const double*)w.nrm, V,
+                         d, w.chosen, m, c, w.w, w.used);
+    else
+      hipLaunchKernelGGL(k_km_weights<0>, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, E, (const double*)w.nrm, V,
+                         d, w.chosen, m, c, w.w, w.used);
+  };
+  weights(0);
   KM_CHECK();
   for (int m = 1; m < c; ++m) {
-    hipLaunchKernelGGL(k_km_draw, dim3(1), dim3(1024), 0, st, (const double*)w.w, V, uni(m), w.chosen, m, w.used);
-    hipLaunchKernelGGL(k_km_weights, dim3(blocks(V, wpb)), dim3(kKmThreads), 0, st, (const double*)w.En, V, d,
-                       (const int32_t*)w.chosen, m, w.w);
+    size_t tb = w.tmp_bytes;
+    if ((e = hipcub::DeviceScan::InclusiveSum(w.tmp, tb, (const double*)w.w, w.sbest, V, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_km_draw, dim3(blocks(V, kKmThreads)), dim3(kKmThreads), 0, st, (const double*)w.sbest, V,
+                       uni(m), w.chosen, m, (const uint8_t*)w.used);
+    weights(m);
     KM_CHECK();
   }
   hipLaunchKernelGGL(k_km_gather_rows, dim3(blocks(c, wpb)), dim3(kKmThreads), 0, st, (const double*)w.En,
@@ -525,9 +586,22 @@ hipError_t launch_build_clusters(int V, int d, int c, int src_bf16, const void* 
     if (n_ev > 0) {
       hipLaunchKernelGGL(k_km_topm, dim3(blocks(n_ev, wpb)), dim3(kKmThreads), 0, st, (const double*)w.En,
                          (const double*)w.Cn, (const int32_t*)w.ev, n_ev, c, d, w.top);
-      hipLaunchKernelGGL(k_km_repair, dim3(1), dim3(64), 0, st, (const double*)w.En, (const double*)w.Cn,
-                         (const int32_t*)w.ev, n_ev, (const int32_t*)w.top, (const int32_t*)w.room, c, d, w.a);
-      KM_CHECK();
+      const int g = blocks(c, kKmThreads / 64) < kRescanWG ? blocks(c, kKmThreads / 64) : kRescanWG;
+      for (int pos = 0;;) {
+        hipLaunchKernelGGL(k_km_repair, dim3(1), dim3(64), 0, st, (const int32_t*)w.ev, n_ev, pos,
+                           (const int32_t*)w.top, w.room, c, w.a, w.status);
+        KM_CHECK();
+        if ((e = hipMemcpyAsync(&pos, w.status, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+        if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+        if (pos >= n_ev) break;
+        hipLaunchKernelGGL(k_km_rescan, dim3(g), dim3(kKmThreads), 0, st, (const double*)w.En, (const double*)w.Cn,
+                           (const int32_t*)w.ev, (const int32_t*)w.status, (const int32_t*)w.room, c, d, w.part_v,
+                           w.part_k);
+        hipLaunchKernelGGL(k_km_place, dim3(1), dim3(64), 0, st, (const double*)w.part_v, (const int32_t*)w.part_k,
+                           g, (const int32_t*)w.ev, (const int32_t*)w.status, c, w.room, w.a);
+        KM_CHECK();
+        ++pos;
+      }
     }
     // members of every cluster in ascending token id
     hipLaunchKernelGGL(k_km_iota_cluster, dim3(blocks(V, 256)), dim3(256), 0, st, (const int32_t*)w.a, V, w.key32,

@@ -75,6 +75,23 @@ def test_mid_size_invariants_and_determinism(gpu):
     assert np.array_equal(C1, kmeans.centroids_from_c2t(ohead.decode(hd.E, "bf16"), T1, "bf16"))
 
 
+@pytest.mark.parametrize("name", ["llama", "gemma", "qwen", "int4"])
+def test_full_size_clusterings_match_the_oracle(gpu, name):
+    """The four large heads (V up to 262144, c up to 16384, 10 iterations): the GPU clustering
+    equals the one the oracle wrote to tests/golden, every cluster."""
+    wl, hd, C2T_ref, _ = H.load(name)
+    desc = fh.make_desc(1, wl.d, wl.V, wl.c, wl.dtype, wl.dtype, wl.dtype)
+    ws = torch.empty(fh.flashhead_build_clusters_workspace_bytes(desc, wl.dtype), dtype=torch.uint8, device=gpu)
+    cent = torch.empty(wl.c * wl.d, dtype=torch.int16, device=gpu)
+    c2t = torch.empty(wl.V, dtype=torch.int32, device=gpu)
+    fh.flashhead_build_clusters(desc, wl.dtype, to_device(hd.E, gpu), wl.kmeans_iters, wl.data_seed, False, cent,
+                                c2t, ws)
+    torch.cuda.synchronize()
+    C2T = c2t.cpu().numpy().reshape(wl.c, wl.V // wl.c)
+    _check_balanced(C2T, wl.V, wl.c)
+    assert np.array_equal(C2T, C2T_ref), f"{np.mean(np.any(C2T != C2T_ref, axis=1)):.4%} of the clusters differ"
+
+
 def test_rejects_bad_arguments(gpu):
     desc = fh.make_desc(1, 64, 4096, 256, "f32", "f32", "f32")
     ws = torch.empty(16, dtype=torch.uint8, device=gpu)
