@@ -22,12 +22,16 @@ struct Sampling {
   uint64_t seed, step;
 };
 
+// Per-row packed maxima are kBestStride uint64 apart (one 128-byte line per row), so the
+// atomic maxima of different rows never contend for a cache line.
+constexpr int kBestStride = 16;
+
 // Workspace carve-up (all offsets 256-byte aligned): keys, masks, best, probes; the
 // regions stage 1 writes come first so their offsets do not depend on p.
 struct Workspace {
   float* keys;        // [B][c] stage-1 keys
   int32_t* probes;    // [B][p] kept clusters, ascending
-  uint64_t* best;     // [B] packed (key, ~token) maxima
+  uint64_t* best;     // [B][kBestStride] packed (key, ~token) maxima (element 0 of each line)
   uint64_t* part;     // [256] per-workgroup maxima of the fused B = 1 stage 2
   uint64_t* mask;     // [c][W] rows that kept cluster k (B > 1 only), W = ceil(B / 64)
   int W;

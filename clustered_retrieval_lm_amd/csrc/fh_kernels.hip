@@ -229,8 +229,83 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
     o = __shfl_xor(bc, 32, kWave);
     bc = o > bc ? o : bc;
     const int n = n0 + 16 * wave + lane;
-    if (lane < 16 && n < a.B) atomicMax((unsigned long long*)&a.best[n], (unsigned long long)bc);
+    if (lane < 16 && n < a.B) atomicMax((unsigned long long*)&a.best[(size_t)n * kBestStride], (unsigned long long)bc);
   }
+}
+
+// Eight consecutive elements of h (bf16 or fp32 storage) from byte address src as floats;
+// zeros if !ok (src must still be a readable address: the load is unconditional).
+__device__ __forceinline__ void h_piece8(float (&hv)[8], const char* src, int h_bf16, bool ok) {
+  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  if (h_bf16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {x.x & m, x.y & m, x.z & m, x.w & m};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { hv[2 * j] = bf16_lo(w[j]); hv[2 * j + 1] = bf16_hi(w[j]); }
+  } else {
+    const uint4 x = reinterpret_cast<const uint4*>(src)[0];
+    const uint4 y = reinterpret_cast<const uint4*>(src)[1];
+    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hv[j] = __uint_as_float(w[j] & m);
+  }
+}
+
+// rows_dot with h read from memory (L2) piece by piece instead of held in registers: the same
+// fused multiply-adds in the same order per row, so the results are bitwise those of rows_dot
+// with load_h.  For kernels that dot the same rows with many hidden states.
+template <int RF, int CH, int NR>
+__device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, const void* h, int h_bf16, int d,
+                                                int lane, float (&out)[NR]) {
+  constexpr int EPC = Fmt<RF>::EPC;
+  const int esz = h_bf16 ? 2 : 4;
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int e0 = (lane + kWave * i) * EPC;
+    const bool ok = e0 < d;
+    const char* src = (const char*)h + (ok ? (size_t)e0 * esz : 0);
+    if (RF == RF_F32) {
+      float hv[4];
+      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      if (h_bf16) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        hv[0] = bf16_lo(x.x & m); hv[1] = bf16_hi(x.x & m); hv[2] = bf16_lo(x.y & m); hv[3] = bf16_hi(x.y & m);
+      } else {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        hv[0] = __uint_as_float(x.x & m); hv[1] = __uint_as_float(x.y & m);
+        hv[2] = __uint_as_float(x.z & m); hv[3] = __uint_as_float(x.w & m);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_F32>(g.w[r][i], hv, acc[r], 0.f);
+    } else if (RF == RF_BF16) {
+      float hv[8];
+      h_piece8(hv, src, h_bf16, ok);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_BF16>(g.w[r][i], hv, acc[r], 0.f);
+    } else {
+      float s[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {             // word j of the row chunk: elements 8 j .. 8 j + 7
+        float hv[8];
+        h_piece8(hv, src + (size_t)8 * j * esz, h_bf16, ok);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t wj = j == 0 ? g.w[r][i].x : j == 1 ? g.w[r][i].y : j == 2 ? g.w[r][i].z : g.w[r][i].w;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s[r] = fmaf(nib(wj, k), hv[k], s[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = fmaf(__uint_as_float(g.sc[r][i] << 16), s[r], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[r] = wave_sum(acc[r]);
 }
 
 // ------------------------------------------------------------------ probe selection
@@ -256,7 +331,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
     if (probe_out) probe_out[(size_t)r * p + q] = k;
     if (mask) atomicOr((unsigned long long*)&mask[(size_t)k * W + (r >> 6)], 1ull << (r & 63));
   }
-  if (tid == 0) best[r] = 0ull;
+  if (tid == 0) best[(size_t)r * kBestStride] = 0ull;
 }
 
 // ------------------------------------------------------------------ B = 1 fused path
@@ -753,9 +828,14 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
   const int hsz = a.h_bf16 ? 2 : 4;
+  const bool want = a.logits_out || a.tokens_out;
   const char* tile = a.tiles + (size_t)k * a.b * rb;
   const uint16_t* sc = RF == RF_INT4 ? a.scales + (size_t)k * a.b * spr : nullptr;
-  for (int j0 = wave * kRPI; j0 < a.b; j0 += 4 * kRPI) {
+  __shared__ uint64_t wbest[2][4];
+  int par = 0;
+  // every wave runs the same (block, row) sequence: the barrier below is reached uniformly
+  for (int base = 0; base < a.b; base += 4 * kRPI) {
+    const int j0 = base + wave * kRPI;              // may lie past the tile: no candidates
     RowGroup<RF, CH> g;
     rows_load<RF, CH>(g, tile, rb, j0, a.b, sc, spr, lane);
     int tj[kRPI];
@@ -767,16 +847,27 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
         const int r = wi * 64 + __builtin_ctzll(bits);
         bits &= bits - 1ull;
         if (r >= a.B) continue;                   // only if the workspace holds no masks
-        HRegs<RF, CH> hr;
-        load_h<RF, CH>(hr, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane);
+        // the row words are opaque per hidden row: their conversions are redone for each row
+        // instead of being hoisted out of this loop (which would hold every converted element
+        // of the four rows in registers)
+#pragma unroll
+        for (int i = 0; i < kRPI; ++i)
+#pragma unroll
+          for (int q = 0; q < CH; ++q) {
+            asm volatile("" : "+v"(g.w[i][q].x), "+v"(g.w[i][q].y), "+v"(g.w[i][q].z), "+v"(g.w[i][q].w));
+            asm volatile("" : "+v"(g.sc[i][q]));
+          }
         float z[kRPI];
-        rows_dot<RF, CH>(g, hr, z);
-        // position of k in row r's ascending probe list
-        const int32_t* pr = a.probes + (size_t)r * a.p;
-        int lo = 0, hi = a.p;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (pr[mid] < k) lo = mid + 1; else hi = mid;
+        rows_dot_stream<RF, CH>(g, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane, z);
+        // position of k in row r's ascending probe list (probe outputs only)
+        int lo = 0;
+        if (want) {
+          const int32_t* pr = a.probes + (size_t)r * a.p;
+          int hi = a.p;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (pr[mid] < k) lo = mid + 1; else hi = mid;
+          }
         }
         uint64_t bc = 0;
 #pragma unroll
@@ -791,8 +882,16 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
             if (a.tokens_out) a.tokens_out[o] = t;
           }
         }
+        // the four waves' maxima for row r meet in LDS: one atomic per (cluster, row)
         bc = wave_max_u64(bc);
-        if (lane == 0) atomicMax((unsigned long long*)&a.best[r], (unsigned long long)bc);
+        if (lane == 0) wbest[par][wave] = bc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          uint64_t m = wbest[par][0];
+          for (int w = 1; w < 4; ++w) m = wbest[par][w] > m ? wbest[par][w] : m;
+          atomicMax((unsigned long long*)&a.best[(size_t)r * kBestStride], (unsigned long long)m);
+        }
+        par ^= 1;
       }
     }
   }
@@ -803,8 +902,8 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
 __global__ void k_finalize(uint64_t* best, int32_t* token, int B) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < B) {
-    token[i] = (int32_t)cand_id(best[i]);
-    best[i] = 0ull;
+    token[i] = (int32_t)cand_id(best[(size_t)i * kBestStride]);
+    best[(size_t)i * kBestStride] = 0ull;
   }
 }
 
@@ -859,7 +958,7 @@ __global__ __launch_bounds__(kThreads) void k_dense_gemv(DenseParams a) {
   if (threadIdx.x == 0) {
     uint64_t m = wmax[0];
     for (int w = 1; w < 4; ++w) m = wmax[w] > m ? wmax[w] : m;
-    atomicMax((unsigned long long*)&a.best[r], (unsigned long long)m);
+    atomicMax((unsigned long long*)&a.best[(size_t)r * kBestStride], (unsigned long long)m);
   }
 }
 
@@ -1037,7 +1136,7 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
     off = up(off + (size_t)c * w.W * sizeof(uint64_t));
   }
   w.best = (uint64_t*)(b ? b + off : nullptr);
-  off = up(off + (size_t)B * sizeof(uint64_t));
+  off = up(off + (size_t)B * kBestStride * sizeof(uint64_t));
   w.part = (uint64_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)kB1Workgroups * sizeof(uint64_t));
   w.probes = (int32_t*)(b ? b + off : nullptr);
@@ -1046,7 +1145,7 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   return w;
 }
 
-size_t dense_workspace_bytes(int B) { return (((size_t)B * sizeof(uint64_t)) + 255) & ~(size_t)255; }
+size_t dense_workspace_bytes(int B) { return (((size_t)B * kBestStride * sizeof(uint64_t)) + 255) & ~(size_t)255; }
 
 int max_chunk_slots(int fmt) { return fmt == RF_INT4 ? 4 : 8; }
 
@@ -1230,7 +1329,8 @@ hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int3
 
 hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E, const Sampling& smp,
                         uint64_t* best, int32_t* token, float* logits, hipStream_t st) {
-  hipLaunchKernelGGL(k_fill_u64, dim3((s.B + 255) / 256), dim3(256), 0, st, best, s.B, (uint64_t)0);
+  hipLaunchKernelGGL(k_fill_u64, dim3((s.B * kBestStride + 255) / 256), dim3(256), 0, st, best, s.B * kBestStride,
+                     (uint64_t)0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const Rng rng = make_rng(smp.seed, smp.step);
