@@ -34,6 +34,9 @@ struct Workspace {
   uint64_t* best;     // [B][kBestStride] packed (key, ~token) maxima (element 0 of each line)
   uint64_t* part;     // [256] per-workgroup maxima of the fused B = 1 stage 2
   uint64_t* mask;     // [c][W] rows that kept cluster k (B > 1 only), W = ceil(B / 64)
+  uint32_t* kflag;    // [c] cluster kept by some row (B > 1 only)
+  int32_t* klist;     // [c] the clusters kept by any row, in no particular order (B > 1 only)
+  int32_t* nkept;     // [1] their count (B > 1 only)
   int W;
   size_t bytes;
 };

@@ -3,7 +3,8 @@
 // Stage 1  k_scores_gemv / k_mfma<EPI_KEYS>  centroid logits C h -> probe keys
 // Select   k_select                           per-row top-p on order-preserving uint32 keys
 // Stage 2  k_tiles_probe (B == 1)             streams the kept clusters' contiguous tiles
-//          k_tiles_mask  (B > 1)              one workgroup per cluster kept by any row
+//          k_tiles_mask  (B > 1)              1024 workgroups loop over the list of clusters kept
+//                                             by any row (each kept tile read once)
 // Token    k_finalize                         packed (key, ~id) maxima -> token ids
 // Dense    k_dense_gemv / k_mfma<EPI_ARGMAX>  the full-vocabulary comparator
 // Offline  k_pack / k_check_counts            cluster-major tiles, optional int4 groups
@@ -23,6 +24,7 @@ constexpr int kRPI = 4;          // rows per wave per row-dot step
 constexpr int kB1Threads = 1024; // workgroup size of the B = 1 select + tiles kernel
 constexpr int kB1Workgroups = 256;
 constexpr int kThreads = 256;    // 4 waves
+constexpr int kMaskWorkgroups = 1024;  // k_tiles_mask: workgroups looping over the clusters
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int d) {
   return fmt == RF_F32 ? 4 * d : fmt == RF_BF16 ? 2 * d : d / 2;
@@ -89,6 +91,8 @@ struct ScoreParams {
   float* keys_out;
   uint64_t* mask;
   int W;
+  uint32_t* kflag;
+  int32_t* nkept;
 };
 
 template <int RF, int CH>
@@ -120,11 +124,13 @@ __global__ __launch_bounds__(kThreads) void k_scores_gemv(ScoreParams a) {
         if (a.keys_out) a.keys_out[(size_t)r * a.c + k] = key;
       }
     }
-    if (a.mask && r == 0) {
+    if (a.mask && r == 0) {                      // the selection's per-cluster state, cleared
       for (int j = lane; j < kRPI * a.W; j += kWave) {
         const int k = k0 + j / a.W;
         if (k < a.c) a.mask[(size_t)k * a.W + j % a.W] = 0ull;
       }
+      if (lane < kRPI && k0 + lane < a.c) a.kflag[k0 + lane] = 0u;
+      if (k0 == 0 && lane == 0) *a.nkept = 0;
     }
   }
 }
@@ -149,6 +155,8 @@ struct MfmaParams {
   float* keys_out;
   uint64_t* mask;
   int W;
+  uint32_t* kflag;    // EPI_KEYS, B > 1: the selection's per-cluster flags (cleared here)
+  int32_t* nkept;
   uint64_t* best;     // EPI_ARGMAX: [B]
   float* logits;      // EPI_ARGMAX: [B][rows], may be null
 };
@@ -220,6 +228,8 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
         const int m = m0 + j / a.W;
         if (m < a.rows) a.mask[(size_t)m * a.W + j % a.W] = 0ull;
       }
+      if (threadIdx.x < 16 && m0 + (int)threadIdx.x < a.rows) a.kflag[m0 + threadIdx.x] = 0u;
+      if (m0 == 0 && threadIdx.x == 0) *a.nkept = 0;
     }
     __syncthreads();
   }
@@ -315,9 +325,10 @@ __device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, c
 
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c, int p, int32_t* probes,
                                                         int32_t* probe_out, uint64_t* mask, int W,
-                                                        uint64_t* best) {
+                                                        uint64_t* best, uint32_t* kflag, int32_t* klist,
+                                                        int32_t* nkept) {
   __shared__ SelShared S;
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   uint32_t u[kSelKV][4];
   uint32_t Tu;
   int Tid;
@@ -329,7 +340,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
     const int k = kept_at(S, nwords, q);
     probes[(size_t)r * p + q] = k;
     if (probe_out) probe_out[(size_t)r * p + q] = k;
-    if (mask) atomicOr((unsigned long long*)&mask[(size_t)k * W + (r >> 6)], 1ull << (r & 63));
+    if (mask) {
+      atomicOr((unsigned long long*)&mask[(size_t)k * W + (r >> 6)], 1ull << (r & 63));
+      // the first row to keep k lists it (slots claimed once per wave)
+      const bool first = atomicOr(&kflag[k], 1u) == 0u;
+      const uint64_t bal = __ballot(first);
+      if (bal) {
+        const int leader = __ffsll((unsigned long long)bal) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(nkept, __popcll(bal));
+        base = __shfl(base, leader, kWave);
+        if (first) klist[base + lane_prefix(bal)] = k;
+      }
+    }
   }
   if (tid == 0) best[(size_t)r * kBestStride] = 0ull;
 }
@@ -756,6 +779,8 @@ __global__ __launch_bounds__(256) void k_finalize_parts(const uint64_t* part, in
 // ------------------------------------------------------------------ stage 2
 
 struct TileParams {
+  const int32_t* klist;   // B > 1: the clusters kept by any row ...
+  const int32_t* nkept;   // ... and their count
   const void* h;
   int h_bf16, B, d, c, b, p;
   const int32_t* probes;
@@ -820,78 +845,80 @@ __global__ __launch_bounds__(kThreads) void k_tiles_probe(TileParams a) {
 template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int k = blockIdx.x;
-  const uint64_t* mk = a.mask + (size_t)k * a.W;
-  bool any = false;
-  for (int wi = 0; wi < a.W; ++wi) any |= mk[wi] != 0ull;
-  if (!any) return;
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
   const int hsz = a.h_bf16 ? 2 : 4;
   const bool want = a.logits_out || a.tokens_out;
-  const char* tile = a.tiles + (size_t)k * a.b * rb;
-  const uint16_t* sc = RF == RF_INT4 ? a.scales + (size_t)k * a.b * spr : nullptr;
   __shared__ uint64_t wbest[2][4];
   int par = 0;
-  // every wave runs the same (block, row) sequence: the barrier below is reached uniformly
-  for (int base = 0; base < a.b; base += 4 * kRPI) {
-    const int j0 = base + wave * kRPI;              // may lie past the tile: no candidates
-    RowGroup<RF, CH> g;
-    rows_load<RF, CH>(g, tile, rb, j0, a.b, sc, spr, lane);
-    int tj[kRPI];
+  // workgroup g takes entries g, g + G, ... of the list of clusters kept by any row
+  const int nk = *a.nkept;
+  for (int e = blockIdx.x; e < nk; e += gridDim.x) {
+    const int k = a.klist[e];
+    const uint64_t* mk = a.mask + (size_t)k * a.W;
+    const uint64_t m0 = mk[0];
+    const char* tile = a.tiles + (size_t)k * a.b * rb;
+    const uint16_t* sc = RF == RF_INT4 ? a.scales + (size_t)k * a.b * spr : nullptr;
+    // every wave runs the same (block, row) sequence: the barrier below is reached uniformly
+    for (int base = 0; base < a.b; base += 4 * kRPI) {
+      const int j0 = base + wave * kRPI;            // may lie past the tile: no candidates
+      RowGroup<RF, CH> g;
+      rows_load<RF, CH>(g, tile, rb, j0, a.b, sc, spr, lane);
+      int tj[kRPI];
 #pragma unroll
-    for (int i = 0; i < kRPI; ++i) tj[i] = (j0 + i < a.b) ? a.c2t[(size_t)k * a.b + j0 + i] : 0;
-    for (int wi = 0; wi < a.W; ++wi) {
-      uint64_t bits = mk[wi];
-      while (bits) {
-        const int r = wi * 64 + __builtin_ctzll(bits);
-        bits &= bits - 1ull;
-        if (r >= a.B) continue;                   // only if the workspace holds no masks
-        // the row words are opaque per hidden row: their conversions are redone for each row
-        // instead of being hoisted out of this loop (which would hold every converted element
-        // of the four rows in registers)
+      for (int i = 0; i < kRPI; ++i) tj[i] = (j0 + i < a.b) ? a.c2t[(size_t)k * a.b + j0 + i] : 0;
+      for (int wi = 0; wi < a.W; ++wi) {
+        uint64_t bits = wi == 0 ? m0 : mk[wi];
+        while (bits) {
+          const int r = wi * 64 + __builtin_ctzll(bits);
+          bits &= bits - 1ull;
+          if (r >= a.B) continue;                   // only if the workspace holds no masks
+          // the row words are opaque per hidden row: their conversions are redone for each row
+          // instead of being hoisted out of this loop (which would hold every converted element
+          // of the four rows in registers)
 #pragma unroll
-        for (int i = 0; i < kRPI; ++i)
+          for (int i = 0; i < kRPI; ++i)
 #pragma unroll
-          for (int q = 0; q < CH; ++q) {
-            asm volatile("" : "+v"(g.w[i][q].x), "+v"(g.w[i][q].y), "+v"(g.w[i][q].z), "+v"(g.w[i][q].w));
-            asm volatile("" : "+v"(g.sc[i][q]));
+            for (int q = 0; q < CH; ++q) {
+              asm volatile("" : "+v"(g.w[i][q].x), "+v"(g.w[i][q].y), "+v"(g.w[i][q].z), "+v"(g.w[i][q].w));
+              asm volatile("" : "+v"(g.sc[i][q]));
+            }
+          float z[kRPI];
+          rows_dot_stream<RF, CH>(g, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane, z);
+          // position of k in row r's ascending probe list (probe outputs only)
+          int lo = 0;
+          if (want) {
+            const int32_t* pr = a.probes + (size_t)r * a.p;
+            int hi = a.p;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (pr[mid] < k) lo = mid + 1; else hi = mid;
+            }
           }
-        float z[kRPI];
-        rows_dot_stream<RF, CH>(g, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane, z);
-        // position of k in row r's ascending probe list (probe outputs only)
-        int lo = 0;
-        if (want) {
-          const int32_t* pr = a.probes + (size_t)r * a.p;
-          int hi = a.p;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (pr[mid] < k) lo = mid + 1; else hi = mid;
-          }
-        }
-        uint64_t bc = 0;
+          uint64_t bc = 0;
 #pragma unroll
-        for (int i = 0; i < kRPI; ++i) {
-          const int j = j0 + i;
-          if (lane == i && j < a.b) {
-            const int t = tj[i];
-            const float key = make_key(z[i], a.sample, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
-            bc = pack_cand(key, (uint32_t)t);
-            const size_t o = ((size_t)r * a.p + lo) * a.b + j;
-            if (a.logits_out) a.logits_out[o] = z[i];
-            if (a.tokens_out) a.tokens_out[o] = t;
+          for (int i = 0; i < kRPI; ++i) {
+            const int j = j0 + i;
+            if (lane == i && j < a.b) {
+              const int t = tj[i];
+              const float key = make_key(z[i], a.sample, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+              bc = pack_cand(key, (uint32_t)t);
+              const size_t o = ((size_t)r * a.p + lo) * a.b + j;
+              if (a.logits_out) a.logits_out[o] = z[i];
+              if (a.tokens_out) a.tokens_out[o] = t;
+            }
           }
+          // the four waves' maxima for row r meet in LDS: one atomic per (cluster, row)
+          bc = wave_max_u64(bc);
+          if (lane == 0) wbest[par][wave] = bc;
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            uint64_t m = wbest[par][0];
+            for (int w = 1; w < 4; ++w) m = wbest[par][w] > m ? wbest[par][w] : m;
+            atomicMax((unsigned long long*)&a.best[(size_t)r * kBestStride], (unsigned long long)m);
+          }
+          par ^= 1;
         }
-        // the four waves' maxima for row r meet in LDS: one atomic per (cluster, row)
-        bc = wave_max_u64(bc);
-        if (lane == 0) wbest[par][wave] = bc;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          uint64_t m = wbest[par][0];
-          for (int w = 1; w < 4; ++w) m = wbest[par][w] > m ? wbest[par][w] : m;
-          atomicMax((unsigned long long*)&a.best[(size_t)r * kBestStride], (unsigned long long)m);
-        }
-        par ^= 1;
       }
     }
   }
@@ -1131,9 +1158,18 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   w.keys = (float*)(b ? b + off : nullptr);
   off = up(off + (B == 1 ? (size_t)b1_key_slots(c) * kB1Threads : (size_t)B * c) * sizeof(float));
   w.mask = nullptr;
+  w.kflag = nullptr;
+  w.klist = nullptr;
+  w.nkept = nullptr;
   if (B > 1) {
     w.mask = (uint64_t*)(b ? b + off : nullptr);
     off = up(off + (size_t)c * w.W * sizeof(uint64_t));
+    w.kflag = (uint32_t*)(b ? b + off : nullptr);
+    off = up(off + (size_t)c * sizeof(uint32_t));
+    w.klist = (int32_t*)(b ? b + off : nullptr);
+    off = up(off + (size_t)c * sizeof(int32_t));
+    w.nkept = (int32_t*)(b ? b + off : nullptr);
+    off = up(off + sizeof(int32_t));
   }
   w.best = (uint64_t*)(b ? b + off : nullptr);
   off = up(off + (size_t)B * kBestStride * sizeof(uint64_t));
@@ -1253,11 +1289,11 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     p.M = (const uint16_t*)C;
     p.B = s.B; p.rows = s.c; p.d = s.d;
     p.sample = smp.sample; p.tau = smp.tau; p.rng = rng;
-    p.keys = ws.keys; p.keys_out = keys_out; p.mask = ws.mask; p.W = ws.W;
+    p.keys = ws.keys; p.keys_out = keys_out; p.mask = ws.mask; p.W = ws.W; p.kflag = ws.kflag; p.nkept = ws.nkept;
     return launch_mfma<EPI_KEYS>(p, 1 << 30, st);
   }
   ScoreParams a{h, (const char*)C, c_scales, s.h_bf16, s.B, s.c, s.d, smp.sample, smp.tau, rng,
-                ws.keys, keys_out, ws.mask, ws.W};
+                ws.keys, keys_out, ws.mask, ws.W, ws.kflag, ws.nkept};
   const int groups = (s.c + kRPI - 1) / kRPI;
   int wgs = (groups + 3) / 4;
   if (wgs > 4096) wgs = 4096;
@@ -1276,7 +1312,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
 hipError_t launch_select(const HeadShape& s, int p, const Workspace& ws, int32_t* probe_out, hipStream_t st) {
   hipLaunchKernelGGL(k_select, dim3(s.B), dim3(kSelThreads), 0, st,
                      (const float*)ws.keys, s.c, p,
-                     ws.probes, probe_out, ws.mask, ws.W, ws.best);
+                     ws.probes, probe_out, ws.mask, ws.W, ws.best, ws.kflag, ws.klist, ws.nkept);
   return hipGetLastError();
 }
 
@@ -1288,9 +1324,10 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
   a.probes = ws.probes; a.c2t = c2t; a.tiles = (const char*)tiles; a.scales = scales;
   a.sample = smp.sample; a.tau = smp.tau; a.rng = make_rng(smp.seed, smp.step);
   a.logits_out = logits_out; a.tokens_out = tokens_out; a.best = ws.best; a.mask = ws.mask; a.W = ws.W;
+  a.klist = ws.klist; a.nkept = ws.nkept;
   const int ch = chunk_slots(s.e_fmt, s.d);
   const bool b1 = s.B == 1;
-  const dim3 grid(b1 ? p : s.c);
+  const dim3 grid(b1 ? p : (s.c < kMaskWorkgroups ? s.c : kMaskWorkgroups));
   if (s.e_fmt == RF_F32) {
     if (b1) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_probe<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a)); }
     else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a)); }

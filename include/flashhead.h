@@ -196,7 +196,9 @@ fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const vo
  * keys (ties to the smaller cluster id).  With sampling keys this is Gumbel-top-p, i.e. p
  * clusters drawn without replacement from softmax(s / tau).  Reads the keys the last
  * flashhead_centroid_scores call left in `workspace`; writes the kept ids, ascending, to
- * the workspace and, if probe_ids_out (device, int32 [B][p]) is non-NULL, there too.
+ * the workspace and, if probe_ids_out (device, int32 [B][p]) is non-NULL, there too.  At
+ * B > 1 the selection also records, per cluster, the rows that kept it; that state is
+ * cleared by flashhead_centroid_scores, so each selection needs its own stage-1 call.
  */
 fh_status flashhead_select_probes(const fh_desc* desc, int64_t p, void* workspace,
                                   size_t workspace_bytes, int32_t* probe_ids_out, void* stream);
