@@ -186,14 +186,31 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
     f32x4_t acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = wave; s < nsteps; s += 4) {
-      const int ko = s * 32;
-      const uint4 av = mv ? ld16(mp + ko) : make_uint4(0u, 0u, 0u, 0u);
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, av);
+    // this wave's K steps s = wave, wave + 4, ... in groups of GS: the loads of a group are
+    // all issued (from valid addresses, masked afterwards) before its MFMAs, so one memory
+    // latency is paid per group instead of per step; the MFMA order is unchanged
+    constexpr int GS = NT >= 3 ? 2 : 4;             // steps per group (register budget)
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+    for (int s0 = wave; s0 < nsteps; s0 += 4 * GS) {
+      uint4 av[GS], bv[GS][NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint4 bv = hv[t] ? ld16(hp[t] + ko) : make_uint4(0u, 0u, 0u, 0u);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, bv), acc[t], 0, 0, 0);
+      for (int u = 0; u < GS; ++u) {
+        const int s = s0 + 4 * u;
+        const int ko = s < nsteps ? s * 32 : 0;
+        av[u] = ld16(mp + ko);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bv[u][t] = ld16(hp[t] + ko);
+      }
+#pragma unroll
+      for (int u = 0; u < GS; ++u) {
+        const bool ok = s0 + 4 * u < nsteps;
+        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ok && mv ? av[u] : z4);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (!ok) continue;                        // wave-uniform
+          const uint4 b = hv[t] ? bv[u][t] : z4;
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+        }
       }
     }
 #pragma unroll
@@ -323,18 +340,20 @@ __device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, c
 // uint32; select_regs finds the p-th largest (ties to the smaller id) and the kept ids are
 // written in ascending order (prefix popcounts of a bitmap over the clusters).
 
+// KV: key blocks of four per thread, the smallest power of two with 4 KV NT >= c.
+template <int KV>
 __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c, int p, int32_t* probes,
                                                         int32_t* probe_out, uint64_t* mask, int W,
                                                         uint64_t* best, uint32_t* kflag, int32_t* klist,
                                                         int32_t* nkept) {
   __shared__ SelShared S;
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  uint32_t u[kSelKV][4];
+  uint32_t u[KV][4];
   uint32_t Tu;
   int Tid;
-  load_keys<kSelKV>(keys + (size_t)r * c, c, u, S);
-  select_regs<kSelKV>(u, c, p, S, Tu, Tid);
-  mark_kept<kSelKV>(u, c, Tu, Tid, S);
+  load_keys<KV>(keys + (size_t)r * c, c, u, S);
+  select_regs<KV>(u, c, p, S, Tu, Tid);
+  mark_kept<KV>(u, c, Tu, Tid, S);
   const int nwords = (c + 31) >> 5;
   for (int q = tid; q < p; q += kSelThreads) {
     const int k = kept_at(S, nwords, q);
@@ -1310,9 +1329,14 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
 }
 
 hipError_t launch_select(const HeadShape& s, int p, const Workspace& ws, int32_t* probe_out, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(s.B), dim3(kSelThreads), 0, st,
-                     (const float*)ws.keys, s.c, p,
-                     ws.probes, probe_out, ws.mask, ws.W, ws.best, ws.kflag, ws.klist, ws.nkept);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(s.B), dim3(kSelThreads), 0, st, (const float*)ws.keys, s.c, p, ws.probes,
+                       probe_out, ws.mask, ws.W, ws.best, ws.kflag, ws.klist, ws.nkept);
+  };
+  if (s.c <= 4 * kSelThreads) go(k_select<1>);
+  else if (s.c <= 8 * kSelThreads) go(k_select<2>);
+  else if (s.c <= 16 * kSelThreads) go(k_select<4>);
+  else go(k_select<8>);
   return hipGetLastError();
 }
 

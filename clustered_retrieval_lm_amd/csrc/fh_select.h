@@ -57,7 +57,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
 // the ascending-id rank of every kept cluster.
 constexpr int kSelBins = 2048;
 constexpr int kCand = 256;
-constexpr int kSelKV = 8;                  // uint4 of keys per thread: c <= 32 NT
 constexpr int kMaxWords = 32768 / 32;
 
 struct SelShared {
