@@ -251,6 +251,7 @@ def main() -> int:
     dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.c_dtype, wl.e_pack, wl.dtype,
                                    device="cuda", keep_dense=not args.no_dense)
     c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, wl.B)
+    union_frac = None
     R = args.rotate or max(2, int(np.ceil(4 * MALL_BYTES / max(alg_bytes, 1))))
     log(f"rotating {R} copies of the centroids ({R * dev.C.numel() * dev.C.element_size() / 2**30:.2f} GiB) "
         f"and {R} hidden states over one tile array ({dev.tiles.numel() / 2**30:.2f} GiB)")
@@ -265,6 +266,21 @@ def main() -> int:
     out = dev.outputs(B, p, probes=False)
     fo = fh.make_outputs(out["token"])
     tau = wl.temperatures[0] if (args.mode == "sample" and wl.temperatures) else 1.0
+    if B > 1:
+        # at B > 1 each kept tile is read once for all rows that kept it: the bytes a call must
+        # read are the union of the rows' probe sets (measured here on the R hidden states)
+        ids = torch.empty(B, p, dtype=torch.int32, device="cuda")
+        sizes = []
+        for r in range(R):
+            fh.flashhead_centroid_scores(desc, Hs[r], Cs[r], args.mode, tau, wl.sample_seed, r, ws)
+            fh.flashhead_select_probes(desc, p, ws, ids)
+            sizes.append(int(torch.unique(ids).numel()))
+        union = float(np.mean(sizes))
+        union_frac = union / (B * p)
+        row_b = tile_bytes // (B * p * wl.b)
+        tile_bytes = int(round(union * wl.b * row_b))
+        alg_bytes = c_bytes + tile_bytes + B * wl.d * (4 if wl.dtype == "f32" else 2)
+        log(f"B={B}: {union:.0f} distinct clusters kept per call on average ({B * p} probes)")
     lib = fh.load_library()
     wsb = ws.numel()
     import ctypes
@@ -395,11 +411,18 @@ def main() -> int:
         cpu = cpu_baseline(wl, hd, C2T)
         log(f"oracle: {cpu['value']:.2f} calls/s on {cpu['cores']} threads")
 
-    units = {
-        "k_b1_scores (centroid scores)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
-        "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
-            (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
-    }
+    if B == 1:
+        units = {
+            "k_b1_scores (centroid scores)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
+            "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
+                (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
+        }
+    else:
+        units = {
+            "k_mfma / k_scores_gemv (centroid scores)": (sc_bytes, t_sc, ["fh::k_mfma", "fh::k_scores_gemv"]),
+            "k_select + k_tiles_mask + k_finalize (selection, probe logits, tokens)":
+                (s2_bytes, t_s2, ["fh::k_select", "fh::k_tiles_mask", "fh::k_finalize"]),
+        }
     dom = max(units, key=lambda k: units[k][1])
     dom_bytes, dom_t, dom_kernels = units[dom]
     dom_gbs = dom_bytes / dom_t / 1e9
@@ -422,6 +445,12 @@ def main() -> int:
                    "mode": args.mode, "rotated_copies": R},
         "achieved_GBps": round(alg_bytes / t_call / 1e9, 1),
         "algorithmic_bytes": alg_bytes,
+        "kept_union_fraction": None if union_frac is None else round(union_frac, 4),
+        # the batched centroid GEMM on MFMA (B > 1, bf16): its arithmetic rate against the dense
+        # bf16 MFMA peak (it is bound by the centroid bytes: B flop per byte read)
+        "stage1_mfma": None if B == 1 else {
+            "tflops": round(2.0 * B * wl.c * wl.d / t_sc / 1e12, 2), "peak_tflops": 2500.0,
+            "frac": round(2.0 * B * wl.c * wl.d / t_sc / 1e12 / 2500.0, 5)},
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
