@@ -861,7 +861,9 @@ __global__ __launch_bounds__(kThreads) void k_tiles_probe(TileParams a) {
 
 // B > 1: workgroup k serves every row whose probe set holds cluster k; each tile row
 // group is read from HBM once and reused from registers for those rows.
-template <int RF, int CH>
+// SAMPLE: the token keys carry Gumbel noise (the greedy instantiation leaves out the Philox
+// code and its registers).
+template <int RF, int CH, bool SAMPLE>
 __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rb = row_bytes_of(RF, a.d);
@@ -920,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
             const int j = j0 + i;
             if (lane == i && j < a.b) {
               const int t = tj[i];
-              const float key = make_key(z[i], a.sample, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+              const float key = make_key(z[i], SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
               bc = pack_cand(key, (uint32_t)t);
               const size_t o = ((size_t)r * a.p + lo) * a.b + j;
               if (a.logits_out) a.logits_out[o] = z[i];
@@ -1354,13 +1356,16 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
   const dim3 grid(b1 ? p : (s.c < kMaskWorkgroups ? s.c : kMaskWorkgroups));
   if (s.e_fmt == RF_F32) {
     if (b1) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_probe<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a)); }
-    else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a)); }
+    else if (smp.sample) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_F32, kCH, true>), grid, dim3(kThreads), 0, st, a)); }
+    else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_F32, kCH, false>), grid, dim3(kThreads), 0, st, a)); }
   } else if (s.e_fmt == RF_BF16) {
     if (b1) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_probe<RF_BF16, kCH>), grid, dim3(kThreads), 0, st, a)); }
-    else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH>), grid, dim3(kThreads), 0, st, a)); }
+    else if (smp.sample) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, true>), grid, dim3(kThreads), 0, st, a)); }
+    else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, false>), grid, dim3(kThreads), 0, st, a)); }
   } else {
     if (b1) { FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_tiles_probe<RF_INT4, kCH>), grid, dim3(kThreads), 0, st, a)); }
-    else    { FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_tiles_mask<RF_INT4, kCH>), grid, dim3(kThreads), 0, st, a)); }
+    else if (smp.sample) { FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_tiles_mask<RF_INT4, kCH, true>), grid, dim3(kThreads), 0, st, a)); }
+    else    { FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_tiles_mask<RF_INT4, kCH, false>), grid, dim3(kThreads), 0, st, a)); }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
