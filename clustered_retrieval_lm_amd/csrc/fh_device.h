@@ -165,6 +165,21 @@ __device__ __forceinline__ float wave_minmax_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// v[lane] for lanes < N (v wave-uniform), v[0] elsewhere: lets lane i handle element i with one
+// evaluation of what follows instead of N evaluations with one lane active each.  The empty asm
+// keeps the selects as selects: rewritten as an indexed load from v, the array would be moved to
+// LDS (4 KB per workgroup, and the work-item ids set up to address it).
+template <int N, typename T>
+__device__ __forceinline__ T lane_pick(const T (&v)[N], int lane) {
+  T x = v[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) {
+    x = lane == i ? v[i] : x;
+    asm volatile("" : "+v"(x));
+  }
+  return x;
+}
+
 __device__ __forceinline__ int lane_prefix(uint64_t bal) {   // set bits of bal below this lane
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }

@@ -115,11 +115,11 @@ __global__ __launch_bounds__(kThreads) void k_scores_gemv(ScoreParams a) {
       rows_load<RF, CH>(g, a.C, rb, k0, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
     float s[kRPI];
     rows_dot<RF, CH>(g, hr, s);
-#pragma unroll
-    for (int i = 0; i < kRPI; ++i) {
-      const int k = k0 + i;
-      if (lane == i && k < a.c) {
-        const float key = make_key(s[i], a.sample, a.tau, a.rng, (uint32_t)r, 0u, (uint32_t)k);
+    {                                            // lane i < kRPI: the key of row k0 + i
+      const float si = lane_pick<kRPI>(s, lane);
+      const int k = k0 + lane;
+      if (lane < kRPI && k < a.c) {
+        const float key = make_key(si, a.sample, a.tau, a.rng, (uint32_t)r, 0u, (uint32_t)k);
         a.keys[(size_t)r * a.c + k] = key;
         if (a.keys_out) a.keys_out[(size_t)r * a.c + k] = key;
       }
@@ -222,16 +222,19 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
       const int n = n0 + 16 * t + (lane & 15);
       const int mb = m0 + 4 * (lane >> 4);
       if (n < a.B) {
+        // the four elements m = mb .. mb + 3 (mb % 4 == 0) share one Philox block
+        const uint4 wb = a.sample ? rng_block(a.rng, (uint32_t)n, EPI == EPI_KEYS ? 0u : 1u, (uint32_t)mb >> 2)
+                                  : make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t wv[4] = {wb.x, wb.y, wb.z, wb.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = mb + i;
           if (m < a.rows) {
+            const float key = a.sample ? sample_key(v[i], a.tau, wv[i]) : v[i] + 0.0f;
             if (EPI == EPI_KEYS) {
-              const float key = make_key(v[i], a.sample, a.tau, a.rng, (uint32_t)n, 0u, (uint32_t)m);
               a.keys[(size_t)n * a.rows + m] = key;
               if (a.keys_out) a.keys_out[(size_t)n * a.rows + m] = key;
             } else {
-              const float key = make_key(v[i], a.sample, a.tau, a.rng, (uint32_t)n, 1u, (uint32_t)m);
               const uint64_t cnd = pack_cand(key, (uint32_t)m);
               bc = cnd > bc ? cnd : bc;
               if (a.logits) a.logits[(size_t)n * a.rows + m] = v[i];
@@ -425,11 +428,11 @@ __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
       rows_load<RF, CH>(g, a.C, rb, k0, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
     float s[kRPI];
     rows_dot<RF, CH>(g, hr, s);
-#pragma unroll
-    for (int i = 0; i < kRPI; ++i) {
-      const int k = k0 + i;
-      if (lane == i && k < a.c) {
-        const float key = make_key(s[i], a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
+    {                                            // lane i < kRPI: the key of row k0 + i
+      const float si = lane_pick<kRPI>(s, lane);
+      const int k = k0 + lane;
+      if (lane < kRPI && k < a.c) {
+        const float key = make_key(si, a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
         a.keys[k] = key;
         if (a.keys_out) a.keys_out[k] = key;
       }
@@ -836,15 +839,15 @@ __global__ __launch_bounds__(kThreads) void k_tiles_probe(TileParams a) {
     rows_load<RF, CH>(g, tile, rb, j0, a.b, sc, spr, lane);
     float z[kRPI];
     rows_dot<RF, CH>(g, hr, z);
-#pragma unroll
-    for (int i = 0; i < kRPI; ++i) {
-      const int j = j0 + i;
-      if (lane == i && j < a.b) {
+    {                                            // lane i < kRPI: the token of row j0 + i
+      const float zi = lane_pick<kRPI>(z, lane);
+      const int j = j0 + lane;
+      if (lane < kRPI && j < a.b) {
         const int t = a.c2t[(size_t)k * a.b + j];
-        const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
+        const float key = make_key(zi, a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
         const uint64_t cnd = pack_cand(key, (uint32_t)t);
         bc = cnd > bc ? cnd : bc;
-        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = z[i];
+        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = zi;
         if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
       }
     }
@@ -917,15 +920,15 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
             }
           }
           uint64_t bc = 0;
-#pragma unroll
-          for (int i = 0; i < kRPI; ++i) {
-            const int j = j0 + i;
-            if (lane == i && j < a.b) {
-              const int t = tj[i];
-              const float key = make_key(z[i], SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+          {                                          // lane i < kRPI: the token of row j0 + i
+            const float zi = lane_pick<kRPI>(z, lane);
+            const int t = lane_pick<kRPI>(tj, lane);
+            const int j = j0 + lane;
+            if (lane < kRPI && j < a.b) {
+              const float key = make_key(zi, SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
               bc = pack_cand(key, (uint32_t)t);
               const size_t o = ((size_t)r * a.p + lo) * a.b + j;
-              if (a.logits_out) a.logits_out[o] = z[i];
+              if (a.logits_out) a.logits_out[o] = zi;
               if (a.tokens_out) a.tokens_out[o] = t;
             }
           }
@@ -989,14 +992,14 @@ __global__ __launch_bounds__(kThreads) void k_dense_gemv(DenseParams a) {
     rows_load<RF, CH>(g, a.E, rb, t0, a.V, nullptr, 0, lane);
     float z[kRPI];
     rows_dot<RF, CH>(g, hr, z);
-#pragma unroll
-    for (int i = 0; i < kRPI; ++i) {
-      const int t = t0 + i;
-      if (lane == i && t < a.V) {
-        const float key = make_key(z[i], a.sample, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+    {                                            // lane i < kRPI: the token t0 + i
+      const float zi = lane_pick<kRPI>(z, lane);
+      const int t = t0 + lane;
+      if (lane < kRPI && t < a.V) {
+        const float key = make_key(zi, a.sample, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
         const uint64_t cnd = pack_cand(key, (uint32_t)t);
         bc = cnd > bc ? cnd : bc;
-        if (a.logits) a.logits[(size_t)r * a.V + t] = z[i];
+        if (a.logits) a.logits[(size_t)r * a.V + t] = zi;
       }
     }
   }
