@@ -1,6 +1,7 @@
 """GPU parity on degenerate stage-1 keys, where the probe selection must fall back from its
 one-histogram fast path to the general selection: every key equal, a long run of equal
-keys across the p-th place, and p = c.
+keys across the p-th place, p = c, and a few keys far above all the others (the linear
+histogram between the key extremes then puts the p-th key in a bin with thousands of others).
 
 The inputs are built so that every score is computed exactly on both sides (h is zero or a
 one-hot vector, so each dot product has at most one non-zero term).  Ties are then exact,
@@ -90,3 +91,27 @@ def test_p_equals_c(gpu, c, dt):
     H.compare_row(ref, 0, got["probe_ids"][0], got["probe_logits"][0], got["probe_tokens"][0], got["token"][0], c,
                   H.L_stage1(1, dt, dt, d), H.L_gemv(dt, d), False, 1.0, 0, 0, dt == "f32", rep)
     assert ref.token[0] == dense.token[0]
+
+
+@pytest.mark.parametrize("c,p,n_high,dt", [(16384, 512, 150, "bf16"), (8016, 256, 60, "bf16"), (1003, 100, 20, "f32")])
+def test_few_keys_far_above(gpu, c, p, n_high, dt):
+    # n_high < p scores far above the rest: the others share the lowest four bins of the
+    # 2048-bin histogram between the extremes; the kept set is the n_high, then the largest of the rest
+    d, b = 64, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=c + n_high, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    rng = np.random.default_rng(c + p)
+    Cf = np.zeros((c, d))
+    Cf[:, 0] = (np.arange(c) % 61) / 8.0
+    high = rng.choice(c, n_high, replace=False)
+    Cf[high, 0] = 4096.0 + 16.0 * np.arange(n_high)
+    C = _storage(Cf, dt)
+    hf = np.zeros((1, d))
+    hf[0, 0] = 1.0
+    h = _storage(hf, dt)
+    s = ohead.decode(C, dt)[:, 0]
+    low = s[np.setdiff1d(np.arange(c), high)]
+    assert (low.max() - low.min()) * 2048 < 4 * (s.max() - s.min())   # within four bins' width
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
+    assert set(high.tolist()) <= set(got["probe_ids"][0].tolist())
