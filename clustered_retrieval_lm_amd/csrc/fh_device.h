@@ -169,6 +169,31 @@ __device__ __forceinline__ float wave_minmax_f32(float v) {
 // evaluation of what follows instead of N evaluations with one lane active each.  The empty asm
 // keeps the selects as selects: rewritten as an indexed load from v, the array would be moved to
 // LDS (4 KB per workgroup, and the work-item ids set up to address it).
+// Lane L of v takes the wave-uniform value x (v_writelane: one instruction, where a select
+// per lane costs a compare, a move and a select).  The lane is an immediate: a second
+// SGPR operand would break the one-SGPR operand limit.  x is often a ballot still in VCC,
+// just written by a VALU compare; a VALU that reads VCC as a constant operand must follow
+// such a write by at least one wait state, and the compiler inserts none inside inline
+// assembly, hence the s_nop.
+template <int L>
+__device__ __forceinline__ void put_lane_i(uint32_t& v, uint32_t x) {
+  asm volatile("s_nop 1\n\tv_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(x), "i"(L));
+}
+
+// put_lane_i for a lane that is a constant once the caller's loop is unrolled (0 <= lane < 32).
+__device__ __forceinline__ void put_lane(uint32_t& v, uint32_t x, int lane) {
+  switch (lane) {
+#define FH_PUT_LANE(L) case L: put_lane_i<L>(v, x); break;
+    FH_PUT_LANE(0) FH_PUT_LANE(1) FH_PUT_LANE(2) FH_PUT_LANE(3) FH_PUT_LANE(4) FH_PUT_LANE(5) FH_PUT_LANE(6)
+    FH_PUT_LANE(7) FH_PUT_LANE(8) FH_PUT_LANE(9) FH_PUT_LANE(10) FH_PUT_LANE(11) FH_PUT_LANE(12) FH_PUT_LANE(13)
+    FH_PUT_LANE(14) FH_PUT_LANE(15) FH_PUT_LANE(16) FH_PUT_LANE(17) FH_PUT_LANE(18) FH_PUT_LANE(19) FH_PUT_LANE(20)
+    FH_PUT_LANE(21) FH_PUT_LANE(22) FH_PUT_LANE(23) FH_PUT_LANE(24) FH_PUT_LANE(25) FH_PUT_LANE(26) FH_PUT_LANE(27)
+    FH_PUT_LANE(28) FH_PUT_LANE(29) FH_PUT_LANE(30) FH_PUT_LANE(31)
+#undef FH_PUT_LANE
+    default: break;
+  }
+}
+
 template <int N, typename T>
 __device__ __forceinline__ T lane_pick(const T (&v)[N], int lane) {
   T x = v[0];

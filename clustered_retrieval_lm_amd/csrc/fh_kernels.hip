@@ -629,8 +629,8 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const uint64_t m = __ballot(bins[s] > b);
-      wlo = lane == s ? (uint32_t)m : wlo;
-      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
+      put_lane(whi, (uint32_t)(m >> 32), s);
       const uint64_t e = __ballot(bins[s] == b);
       if (e) {
         int base = 0;
@@ -657,8 +657,8 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     for (int s = 0; s < NS; ++s) {
       const float v = a.keys[s * NT + tid];
       const uint64_t m = __ballot(v > T) | __ballot(v == T && s * NT + tid <= Tid);
-      wlo = lane == s ? (uint32_t)m : wlo;
-      whi = lane == s ? (uint32_t)(m >> 32) : whi;
+      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
+      put_lane(whi, (uint32_t)(m >> 32), s);
     }
     if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
     n_def = p;
