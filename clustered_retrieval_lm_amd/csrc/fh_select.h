@@ -77,15 +77,19 @@ __device__ __forceinline__ float ord_to_float(uint32_t u) {
   return __uint_as_float((u & 0x80000000u) ? (u ^ 0x80000000u) : ~u);
 }
 
-template <bool MAX>
-__device__ __forceinline__ uint32_t block_minmax(uint32_t v, uint32_t* wred) {
+// Both extremes over the block with one barrier.
+__device__ __forceinline__ void block_minmax2(uint32_t& vmax, uint32_t& vmin, uint32_t* wmax, uint32_t* wmin) {
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  v = wave_minmax_u32<MAX>(v);
-  if ((threadIdx.x & 63) == 0) wred[wave] = v;
+  vmax = wave_minmax_u32<true>(vmax);
+  vmin = wave_minmax_u32<false>(vmin);
+  if ((threadIdx.x & 63) == 0) { wmax[wave] = vmax; wmin[wave] = vmin; }
   __syncthreads();
-  uint32_t r = wred[0];
-  for (int w = 1; w < nw; ++w) r = MAX ? (wred[w] > r ? wred[w] : r) : (wred[w] < r ? wred[w] : r);
-  return r;
+  vmax = wmax[0];
+  vmin = wmin[0];
+  for (int w = 1; w < nw; ++w) {
+    vmax = wmax[w] > vmax ? wmax[w] : vmax;
+    vmin = wmin[w] < vmin ? wmin[w] : vmin;
+  }
 }
 
 // Exclusive prefix sum over the block (thread order); one barrier.  `wtot` must not be
@@ -145,6 +149,35 @@ __device__ __forceinline__ void load_keys(const float* keys, int c, uint32_t (&u
   for (int i = tid; i < kMaxWords; i += NT) S.bitmap[i] = 0u;
 }
 
+// (Tu, Tid) = the need-th largest, by (u desc, id asc), of the keys `pick` accepts (at most
+// kCand of them).  Expects S.ncand zero and a barrier since.
+template <class Each, class Pick>
+__device__ __forceinline__ void rank_candidates(const Each& each, const Pick& pick, int need, SelShared& S,
+                                                uint32_t& Tu, int& Tid) {
+  const int tid = threadIdx.x, NT = blockDim.x;
+  each([&](uint32_t x, int id) {
+    if (pick(x)) {
+      const int slot = atomicAdd(&S.ncand, 1);
+      if (slot < kCand) { S.cu[slot] = x; S.cid[slot] = id; }
+    }
+  });
+  __syncthreads();
+  const int n = S.ncand < kCand ? S.ncand : kCand;
+  for (int t = tid; t < n; t += NT) {
+    const uint32_t ut = S.cu[t];
+    const int it = S.cid[t];
+    int rank = 0;
+    for (int q = 0; q < n; ++q) {
+      const uint32_t uq = S.cu[q];
+      rank += (uq > ut) || (uq == ut && S.cid[q] < it);
+    }
+    if (rank == need - 1) { S.Tu = ut; S.Tid = it; }
+  }
+  __syncthreads();
+  Tu = S.Tu;
+  Tid = S.Tid;
+}
+
 // The selection restricted to the keys in [ilo, ihi] (order-preserving values): every key
 // above ihi is kept, and the `need` largest of the n_in keys in the interval complete the set
 // (n_in >= need).  `each(f)` calls f(u, id) for every key this thread holds (id < c), in any
@@ -182,10 +215,17 @@ __device__ __forceinline__ void select_interval_each(const Each& each, int c, Se
         acc += hc;
       }
     }
+    if (tid == 0) S.ncand = 0;
     __syncthreads();
     const int b = S.bdig[0];
     need -= S.bdig[1];
     n_in = S.bdig[2];
+    if (n_in <= kCand) {                      // block-uniform: rank bin b's keys straight away
+      rank_candidates(
+          each, [&](uint32_t x) { return x >= ilo && x <= ihi && sel_bin(x, flin, lo_f, inv, ilo, ushift) == b; },
+          need, S, Tu, Tid);
+      return;
+    }
     uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
     each([&](uint32_t x, int) {
       if (x >= ilo && x <= ihi && sel_bin(x, flin, lo_f, inv, ilo, ushift) == b) {
@@ -193,8 +233,9 @@ __device__ __forceinline__ void select_interval_each(const Each& each, int c, Se
         bmin = min(bmin, x);
       }
     });
-    ihi = block_minmax<true>(bmax, S.wred[2 + 2 * (level & 1)]);
-    ilo = block_minmax<false>(bmin, S.wred[3 + 2 * (level & 1)]);
+    block_minmax2(bmax, bmin, S.wred[2 + 2 * (level & 1)], S.wred[3 + 2 * (level & 1)]);
+    ihi = bmax;
+    ilo = bmin;
   }
   // every key with u > ihi is kept; `need` more come from the n_in keys in [ilo, ihi]
   if (n_in == need) {                         // the whole interval is kept
@@ -205,27 +246,7 @@ __device__ __forceinline__ void select_interval_each(const Each& each, int c, Se
   if (n_in <= kCand) {                        // rank the candidates exactly
     if (tid == 0) S.ncand = 0;
     __syncthreads();
-    each([&](uint32_t x, int id) {
-      if (x >= ilo && x <= ihi) {
-        const int slot = atomicAdd(&S.ncand, 1);
-        if (slot < kCand) { S.cu[slot] = x; S.cid[slot] = id; }
-      }
-    });
-    __syncthreads();
-    const int n = S.ncand < kCand ? S.ncand : kCand;
-    for (int t = tid; t < n; t += NT) {
-      const uint32_t ut = S.cu[t];
-      const int it = S.cid[t];
-      int rank = 0;
-      for (int q = 0; q < n; ++q) {
-        const uint32_t uq = S.cu[q];
-        rank += (uq > ut) || (uq == ut && S.cid[q] < it);
-      }
-      if (rank == need - 1) { S.Tu = ut; S.Tid = it; }
-    }
-    __syncthreads();
-    Tu = S.Tu;
-    Tid = S.Tid;
+    rank_candidates(each, [&](uint32_t x) { return x >= ilo && x <= ihi; }, need, S, Tu, Tid);
     return;
   }
   // many equal candidates (ilo == ihi): the need-th of them in id order, via the bitmap
@@ -288,9 +309,8 @@ __device__ __forceinline__ void select_regs(const uint32_t (&u)[KV][4], int c, i
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (idof(j, e) < c) { vmax = max(vmax, u[j][e]); vmin = min(vmin, u[j][e]); }
-  const uint32_t ihi = block_minmax<true>(vmax, S.wred[0]);
-  const uint32_t ilo = block_minmax<false>(vmin, S.wred[1]);
-  select_interval<KV>(u, c, S, ilo, ihi, p, c, Tu, Tid);
+  block_minmax2(vmax, vmin, S.wred[0], S.wred[1]);
+  select_interval<KV>(u, c, S, vmin, vmax, p, c, Tu, Tid);
 }
 
 // Word popcounts of S.bitmap turned into prefix offsets (S.woff), for kept_at.
