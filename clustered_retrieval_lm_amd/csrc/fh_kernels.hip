@@ -3,7 +3,7 @@
 // Stage 1  k_scores_gemv / k_mfma<EPI_KEYS>  centroid logits C h -> probe keys
 // Select   k_select                           per-row top-p on order-preserving uint32 keys
 // Stage 2  k_tiles_probe (B == 1)             streams the kept clusters' contiguous tiles
-//          k_tiles_mask  (B > 1)              1024 workgroups loop over the list of clusters kept
+//          k_tiles_mask  (B > 1)              min(c, 8192) workgroups loop over the list of clusters kept
 //                                             by any row (each kept tile read once)
 // Token    k_finalize                         packed (key, ~id) maxima -> token ids
 // Dense    k_dense_gemv / k_mfma<EPI_ARGMAX>  the full-vocabulary comparator
@@ -24,7 +24,7 @@ constexpr int kRPI = 4;          // rows per wave per row-dot step
 constexpr int kB1Threads = 1024; // workgroup size of the B = 1 select + tiles kernel
 constexpr int kB1Workgroups = 256;
 constexpr int kThreads = 256;    // 4 waves
-constexpr int kMaskWorkgroups = 1024;  // k_tiles_mask: workgroups looping over the clusters
+constexpr int kMaskWorkgroups = 8192;  // k_tiles_mask: workgroups looping over the kept clusters
 
 __host__ __device__ __forceinline__ int row_bytes_of(int fmt, int d) {
   return fmt == RF_F32 ? 4 * d : fmt == RF_BF16 ? 2 * d : d / 2;
