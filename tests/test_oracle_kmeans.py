@@ -149,3 +149,48 @@ def test_kmeanspp_uses_stream_two():
     En /= np.linalg.norm(En, axis=1, keepdims=True)
     first = kmeans.kmeanspp_init(En, 1, seed=11)[0]
     assert first == int(np.floor(philox.uniform(11, 0, 0, 2, 0) * V))
+
+
+def test_unit_centroids_are_normalised_sums_of_unit_rows():
+    """unit=True stores c_k = sum of the members' unit rows, normalised (Section 3.1's centroid).
+
+    Rows with integer coordinates and known norms, so every value is written out by hand:
+    cluster 0 holds (3, 4, 0) (norm 5) and (0, 0, 2) (norm 2): unit rows (0.6, 0.8, 0) and
+    (0, 0, 1), sum (0.6, 0.8, 1), norm sqrt(2).  Cluster 1 holds (0, 5, 12) (norm 13) and
+    (8, 0, 6) (norm 10): unit rows (0, 5/13, 12/13) and (0.8, 0, 0.6).  A raw sum, a mean or
+    a sum of raw rows normalised once would all differ from these.
+    """
+    E = np.array([[3.0, 4.0, 0.0], [0.0, 5.0, 12.0], [0.0, 0.0, 2.0], [8.0, 0.0, 6.0]])
+    C2T = np.array([[0, 2], [1, 3]])
+    s0 = np.array([0.6, 0.8, 1.0])
+    s1 = np.array([0.8, 5.0 / 13.0, 12.0 / 13.0 + 0.6])
+    want = np.stack([s0 / np.sqrt(2.0), s1 / np.sqrt(s1 @ s1)])
+    got = kmeans.centroids_from_c2t(E, C2T, "f32", unit=True)
+    assert np.array_equal(got, want.astype(np.float32))
+    gotb = kmeans.centroids_from_c2t(E, C2T, "bf16", unit=True)
+    assert np.array_equal(gotb, codecs.round_to_bf16(want))
+    # the mean would be (1.5, 2, 1) for cluster 0: the flag really changes the result
+    assert not np.allclose(kmeans.centroids_from_c2t(E, C2T, "f32"), got)
+    # a zero row has no direction: it adds nothing to its cluster's sum
+    E0 = np.array([[3.0, 4.0, 0.0], [0.0, 0.0, 0.0]])
+    got0 = kmeans.centroids_from_c2t(E0, np.array([[0, 1]]), "f32", unit=True)
+    assert np.array_equal(got0, np.array([[0.6, 0.8, 0.0]], dtype=np.float32))
+
+
+def test_build_clusters_unit_stores_the_unit_centroids_of_its_clustering():
+    """build_clusters(unit=True) stores normalise(sum of unit member rows) of the C2T it returns.
+
+    Two tight groups of rows along orthogonal axes (b = 3): the clustering is forced, and the
+    stored centroids must equal the hand-computed normalised sums of the unit rows."""
+    E = np.array([[2.0, 0.1, 0.0], [0.0, 3.0, 0.2], [4.0, 0.0, 0.3], [0.1, 1.0, 0.0],
+                  [1.0, 0.2, 0.1], [0.2, 2.0, 0.1]])
+    stored, C2T = kmeans.build_clusters(E, 2, iters=3, seed=0, unit=True, out_dtype="f32")
+    assert sorted(C2T.tolist()) == [[0, 2, 4], [1, 3, 5]]
+    for k in range(2):
+        g = C2T[k]
+        u = E[g] / np.linalg.norm(E[g], axis=1, keepdims=True)
+        s = u.sum(axis=0)
+        want = (s / np.linalg.norm(s)).astype(np.float32)
+        assert np.allclose(stored[k], want, rtol=0, atol=2.0 ** -23), (k, stored[k], want)
+    # and it agrees with centroids_from_c2t(unit=True) on the returned clustering
+    assert np.allclose(stored, kmeans.centroids_from_c2t(E, C2T, "f32", unit=True), rtol=0, atol=2.0 ** -23)
