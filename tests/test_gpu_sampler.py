@@ -134,5 +134,6 @@ def test_gemma_sampling_1000_steps(gpu):
                           seed, step, False, rep)
             ref_cache[step] = int(ref.token[0])
     print(rep)
+    rep.check_flag_rate()
     # different steps draw different tokens: the sampler is not stuck on one token
     assert len(np.unique(tok)) > 10
