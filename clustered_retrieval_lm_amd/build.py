@@ -12,8 +12,19 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libflashhead.so")
-SOURCES = ["fh_kernels.hip", "fh_cluster.hip", "fh_mc.hip", "fh_api.hip"]
-HEADERS = ["fh_device.h", "fh_internal.h", "fh_select.h"]
+# (source, object name, extra flags): fh_b1.hip is compiled once per row format so that the
+# three formats' B = 1 kernels build in parallel
+SOURCES = [
+    ("fh_kernels.hip", "fh_kernels", []),
+    ("fh_b1.hip", "fh_b1_f32", ["-DFH_B1_RF=0"]),
+    ("fh_b1.hip", "fh_b1_bf16", ["-DFH_B1_RF=1"]),
+    ("fh_b1.hip", "fh_b1_int4", ["-DFH_B1_RF=2"]),
+    ("fh_cluster.hip", "fh_cluster", []),
+    ("fh_mc.hip", "fh_mc", []),
+    ("fh_util.hip", "fh_util", []),
+    ("fh_api.hip", "fh_api", []),
+]
+HEADERS = ["fh_device.h", "fh_internal.h", "fh_rows.h", "fh_select.h"]
 ARCH = os.environ.get("FLASHHEAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -48,13 +59,13 @@ def build(verbose: bool = False) -> str:
     objdir = os.path.join(LIBDIR, "obj")
     os.makedirs(objdir, exist_ok=True)
     objs, procs = [], []
-    for s in SOURCES:
-        obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
-        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, s), "-o", obj]
+    for s, name, extra in SOURCES:
+        obj = os.path.join(objdir, name + ".o")
+        cmd = [hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         objs.append(obj)
-        procs.append((s, _run(cmd)))
+        procs.append((name, _run(cmd)))
     failed, msgs = [], []
     for s, pr in procs:
         out, _ = pr.communicate()

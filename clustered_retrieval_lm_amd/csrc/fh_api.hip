@@ -259,7 +259,10 @@ fh_status flashhead_select_probes(const fh_desc* desc, int64_t p, void* workspac
   if ((st = check_p(desc, p)) != FH_OK) return st;
   fh::Workspace ws;
   if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
-  hipError_t e = fh::launch_select(shape_of(desc), (int)p, ws, probe_ids_out, (hipStream_t)stream);
+  // the B > 1 per-cluster state starts cleared whatever ran on this workspace before
+  hipError_t e = fh::launch_clear_select(ws, (int)desc->c, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "selection state reset");
+  e = fh::launch_select(shape_of(desc), (int)p, ws, probe_ids_out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "probe selection launch");
   return FH_OK;
 }
@@ -294,13 +297,18 @@ fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h, 
 // Probe selection and stage 2: at B = 1 one fused kernel, else the select and tile kernels.
 static fh_status select_and_probe(const fh::HeadShape& s, int p, const void* h, const int32_t* c2t,
                                   const void* tiles, const void* scales, const fh::Sampling& smp,
-                                  const fh::Workspace& ws, const fh_outputs* out, hipStream_t hs) {
+                                  const fh::Workspace& ws, const fh_outputs* out, bool state_clear,
+                                  hipStream_t hs) {
   hipError_t e;
   if (s.B == 1) {
     e = fh::launch_stage2_b1(s, p, h, c2t, tiles, (const uint16_t*)scales, smp, ws, out->probe_ids,
                              out->probe_logits, out->probe_tokens, out->token, hs);
     if (e != hipSuccess) return hip_fail(e, "fused selection and probe logits launch");
     return FH_OK;
+  }
+  if (!state_clear) {           // no stage-1 launch of this call cleared the per-cluster state
+    e = fh::launch_clear_select(ws, s.c, hs);
+    if (e != hipSuccess) return hip_fail(e, "selection state reset");
   }
   e = fh::launch_select(s, p, ws, out->probe_ids, hs);
   if (e != hipSuccess) return hip_fail(e, "probe selection launch");
@@ -322,7 +330,7 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
   fh::Workspace ws;
   if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
   return select_and_probe(shape_of(desc), (int)p, h, cluster_tokens, E_tiles, E_scales,
-                          sampling_of(mode, temperature, seed, step), ws, out, (hipStream_t)stream);
+                          sampling_of(mode, temperature, seed, step), ws, out, false, (hipStream_t)stream);
 }
 
 fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
@@ -342,7 +350,7 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
-  return select_and_probe(s, (int)p, h, cluster_tokens, E_tiles, E_scales, smp, ws, out, hs);
+  return select_and_probe(s, (int)p, h, cluster_tokens, E_tiles, E_scales, smp, ws, out, true, hs);
 }
 
 fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* bytes) {
@@ -382,7 +390,7 @@ fh_status flashhead_mc_marginal(const fh_desc* desc, const void* h, const void* 
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
   if (desc->e_dtype == FH_INT4_G128) {
     const fh_outputs all{w.token, nullptr, w.z, nullptr};
-    if ((st = select_and_probe(s, s.c, h, cluster_tokens, E_tiles, E_scales, plain, w.fw, &all, hs)) != FH_OK)
+    if ((st = select_and_probe(s, s.c, h, cluster_tokens, E_tiles, E_scales, plain, w.fw, &all, true, hs)) != FH_OK)
       return st;
   } else {
     e = fh::launch_dense(s, s.c * s.b, h, E_tiles, plain, w.fw.best, w.token, w.z, hs);
@@ -406,7 +414,6 @@ fh_status flashhead_dense_forward(const fh_desc* desc, const void* h, const void
                                   int32_t* token, float* logits, void* stream) {
   fh_status st = check_desc(desc, false);
   if (st != FH_OK) return st;
-  if (desc->e_dtype == FH_INT4_G128) return fail(FH_ERR_DTYPE, "the dense head takes F32 or BF16 E");
   if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
   if (!h || !E || !token) return fail(FH_ERR_ARG, "h, E and token must be non-NULL");
   if (!workspace) return fail(FH_ERR_WORKSPACE, "workspace is NULL");
@@ -416,6 +423,19 @@ fh_status flashhead_dense_forward(const fh_desc* desc, const void* h, const void
   hipError_t e = fh::launch_dense(shape_of(desc), (int)desc->V, h, E, sampling_of(mode, temperature, seed, step),
                                   (uint64_t*)workspace, token, logits, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "dense head launch");
+  return FH_OK;
+}
+
+fh_status flashhead_philox_words(uint64_t seed, uint32_t row, uint64_t step, uint32_t rng_stream, uint32_t n0,
+                                 int64_t count, uint32_t* words_out, float* gumbel_out, void* stream) {
+  if (rng_stream > 3) return fail(FH_ERR_ARG, "rng_stream=%u must be 0, 1, 2 or 3", (unsigned)rng_stream);
+  if (count < 0 || (uint64_t)n0 + (uint64_t)count > (uint64_t(1) << 32))
+    return fail(FH_ERR_ARG, "count=%lld must be >= 0 with n0 + count <= 2^32", (long long)count);
+  if (!words_out && !gumbel_out) return fail(FH_ERR_ARG, "words_out and gumbel_out are both NULL");
+  if (count == 0) return FH_OK;
+  hipError_t e = fh::launch_philox_words(seed, row, step, rng_stream, n0, count, words_out, gumbel_out,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "philox launch");
   return FH_OK;
 }
 

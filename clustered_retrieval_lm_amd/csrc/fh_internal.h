@@ -26,6 +26,17 @@ struct Sampling {
 // atomic maxima of different rows never contend for a cache line.
 constexpr int kBestStride = 16;
 
+// B = 1: the fused selection + stage 2 runs kB1Threads threads per workgroup, each holding
+// b1_key_slots(c) / kB1Threads keys (a power of two >= 2); the workspace keys are padded to
+// b1_key_slots(c).
+constexpr int kB1Threads = 1024;
+constexpr int kB1Workgroups = 256;
+__host__ __device__ inline int b1_key_slots(int c) {
+  int s = 2;
+  while (s * kB1Threads < c) s *= 2;
+  return s * kB1Threads;
+}
+
 // Workspace carve-up (all offsets 256-byte aligned): keys, masks, best, probes; the
 // regions stage 1 writes come first so their offsets do not depend on p.
 struct Workspace {
@@ -56,6 +67,34 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
                         const void* tiles, const uint16_t* scales, const Sampling& smp,
                         const Workspace& ws, float* logits_out, int32_t* tokens_out,
                         int32_t* token, hipStream_t st);
+// One B = 1 call as the fused kernels (fh_b1.hip) take it.
+struct B1Args {
+  const void* h;
+  const void* C;
+  const uint16_t* c_scales;   // int4 centroids: their scales
+  int h_bf16, c, d, b, p;
+  int sample;
+  float tau;
+  uint64_t seed, step;
+  float* keys;
+  float* keys_out;
+  uint64_t* part;
+  const int32_t* c2t;
+  const void* tiles;
+  const uint16_t* scales;
+  int32_t* probe_out;
+  float* logits_out;
+  int32_t* tokens_out;
+  int32_t* token;
+};
+// fh_b1.hip, one object per row format: stage 1 by the centroids' format, selection + stage 2
+// (+ token) by the tiles' format.
+hipError_t launch_b1_scores_f32(const B1Args& a, hipStream_t st);
+hipError_t launch_b1_scores_bf16(const B1Args& a, hipStream_t st);
+hipError_t launch_b1_scores_int4(const B1Args& a, hipStream_t st);
+hipError_t launch_b1_stage2_f32(const B1Args& a, hipStream_t st);
+hipError_t launch_b1_stage2_bf16(const B1Args& a, hipStream_t st);
+hipError_t launch_b1_stage2_int4(const B1Args& a, hipStream_t st);
 // B = 1 probe selection fused with stage 2 (one kernel, then the token decode); reads the
 // keys launch_scores left in the workspace.
 hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int32_t* c2t, const void* tiles,
@@ -97,6 +136,11 @@ inline size_t int4_scales_offset(size_t rows, size_t d) { return (rows * d / 2 +
 inline size_t int4_rows_bytes(size_t rows, size_t d) { return int4_scales_offset(rows, d) + rows * (d / 128) * 2; }
 hipError_t launch_quant_int4_rows(const uint16_t* src, int rows, int d, uint8_t* q, uint16_t* scales,
                                   hipStream_t st);
+// The sampler's Philox words / fp32 Gumbel values for elements n0 .. n0 + count - 1 (fh_util.hip).
+hipError_t launch_philox_words(uint64_t seed, uint32_t row, uint64_t step, uint32_t stream, uint32_t n0,
+                               int64_t count, uint32_t* words, float* gum, hipStream_t st);
+// B > 1: clears the selection's per-cluster state (row masks, kept flags, kept count).
+hipError_t launch_clear_select(const Workspace& ws, int c, hipStream_t st);
 hipError_t launch_pack(int V, int d, int c, int b, int src_bf16, int dst_fmt, const void* E,
                        const int32_t* c2t, void* tiles, uint16_t* scales, uint32_t* counts,
                        uint32_t* bad, hipStream_t st);

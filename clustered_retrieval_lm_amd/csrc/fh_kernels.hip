@@ -13,69 +13,11 @@
 // Language Model Inference", Section 3.2 (two-stage retrieval, dense C2T).
 #include "fh_device.h"
 #include "fh_internal.h"
+#include "fh_rows.h"
 #include "fh_select.h"
 
 namespace fh {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kRPI = 4;          // rows per wave per row-dot step
-constexpr int kB1Threads = 1024; // workgroup size of the B = 1 select + tiles kernel
-constexpr int kB1Workgroups = 256;
-constexpr int kThreads = 256;    // 4 waves
-constexpr int kMaskWorkgroups = 8192;  // k_tiles_mask: workgroups looping over the kept clusters
-
-__host__ __device__ __forceinline__ int row_bytes_of(int fmt, int d) {
-  return fmt == RF_F32 ? 4 * d : fmt == RF_BF16 ? 2 * d : d / 2;
-}
-
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// Streaming 16-byte load (non-temporal: rows of C, tiles and E are read once per call).
-__device__ __forceinline__ uint4 ld16_stream(const void* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// ------------------------------------------------------------------ row dot products
-
-template <int RF, int CH, int NR = kRPI>
-struct RowGroup {
-  uint4 w[NR][CH];
-  uint32_t sc[NR][CH];      // int4: bf16 bits of the group scale (converted at the dot)
-};
-
-// Load rows [j0, j0 + NR) (those < nrows) of a matrix with row stride rb bytes.
-template <int RF, int CH, int NR>
-__device__ __forceinline__ void rows_load(RowGroup<RF, CH, NR>& g, const char* base, int rb, int j0, int nrows,
-                                          const uint16_t* scales, int spr, int lane) {
-  const int cpr = rb >> 4;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int j = j0 + r;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int q = lane + kWave * i;
-      const bool ok = j < nrows && q < cpr;
-      g.w[r][i] = ok ? ld16_stream(base + (size_t)j * rb + (size_t)q * 16) : make_uint4(0u, 0u, 0u, 0u);
-      g.sc[r][i] = (RF == RF_INT4 && ok) ? (uint32_t)scales[(size_t)j * spr + (q >> 2)] : 0u;
-    }
-  }
-}
-
-// Full dot products of the loaded rows with h (every lane receives every sum).
-template <int RF, int CH, int NR>
-__device__ __forceinline__ void rows_dot(const RowGroup<RF, CH, NR>& g, const HRegs<RF, CH>& hr, float (&out)[NR]) {
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) acc = chunk_dot<RF>(g.w[r][i], hr.v[i], acc, __uint_as_float(g.sc[r][i] << 16));
-    out[r] = wave_sum(acc);
-  }
-}
 
 // ------------------------------------------------------------------ stage 1, row GEMV
 
@@ -138,9 +80,20 @@ __global__ __launch_bounds__(kThreads) void k_scores_gemv(ScoreParams a) {
 // ------------------------------------------------------------------ bf16 MFMA GEMM
 // S[n][m] = sum_k H[n][k] M[m][k] with v_mfma_f32_16x16x32_bf16: A = 16 rows of M
 // (lane l: row l % 16, k = 8 (l / 16) .. +7), B = 16 rows of H (same lane map),
-// D lane l: column n = l % 16, rows m = 4 (l / 16) + i.  A workgroup owns one 16-row tile
-// of M at a time and 64 rows of H; its 4 waves split K (k-steps w, w + 4, ...) and their
-// partial tiles are summed in LDS in wave order.
+// D lane l: column n = l % 16, rows m = 4 (l / 16) + i.
+//
+// A workgroup of kMfmaWaves waves owns kMfmaMT 16-row tiles of M at a time (32 rows) and NT
+// 16-row tiles of H (up to 64 rows); its waves split K: wave w takes the K-steps (32 columns
+// each) w, w + 8, ...  A wave issues the loads of up to GS of its K-steps (the whole range at
+// d = 1024 and NT = 4) before any MFMA, so a tile costs about one memory round trip.  With
+// NACC > 1 a wave rotates NACC accumulators per tile over its K-steps, shortening the rounding
+// chain, and sums them by a tree at the end; the partial tiles of the 8 waves are summed in
+// LDS by a fixed 3-level tree.  Roundings on the path of one product: <= 6 per MFMA (32 exact
+// bf16 products and the accumulator, a tree of depth 6) times ceil(steps per wave / NACC),
+// + log2(NACC), + 3.
+constexpr int kMfmaWaves = 8;
+constexpr int kMfmaMT = 2;
+constexpr int kMfmaThreads = kMfmaWaves * 64;
 
 enum { EPI_KEYS = 0, EPI_ARGMAX = 1 };
 
@@ -162,13 +115,16 @@ struct MfmaParams {
 };
 
 template <int NT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
-  __shared__ f32x4_t red[4][NT][kWave];
+__global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
+  constexpr int MT = kMfmaMT, NW = kMfmaWaves;
+  constexpr int GS = NT >= 3 ? 4 : 8;               // K-steps per load group (register budget)
+  constexpr int NACC = NT == 1 ? 4 : NT == 2 ? 2 : 1;
+  __shared__ f32x4_t red[NW][MT * NT][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = blockIdx.y * 64;
   const int kq = (lane >> 4) * 8;
   const int nsteps = a.d / 32;
-  const int ntiles = (a.rows + 15) / 16;
+  const int ngroups = (a.rows + 16 * MT - 1) / (16 * MT);
   const uint16_t* hp[NT];
   bool hv[NT];
 #pragma unroll
@@ -177,50 +133,67 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
     hv[t] = n < a.B;
     hp[t] = a.H + (size_t)(hv[t] ? n : 0) * a.d + kq;
   }
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
   uint64_t bc = 0;
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int m0 = tile * 16;
-    const int mr = m0 + (lane & 15);
-    const bool mv = mr < a.rows;
-    const uint16_t* mp = a.M + (size_t)(mv ? mr : 0) * a.d + kq;
-    f32x4_t acc[NT];
+  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int m0 = grp * 16 * MT;
+    const uint16_t* mp[MT];
+    bool mv[MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // this wave's K steps s = wave, wave + 4, ... in groups of GS: the loads of a group are
-    // all issued (from valid addresses, masked afterwards) before its MFMAs, so one memory
-    // latency is paid per group instead of per step; the MFMA order is unchanged
-    constexpr int GS = NT >= 3 ? 2 : 4;             // steps per group (register budget)
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * GS) {
-      uint4 av[GS], bv[GS][NT];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int mr = m0 + 16 * mt + (lane & 15);
+      mv[mt] = mr < a.rows;
+      mp[mt] = a.M + (size_t)(mv[mt] ? mr : 0) * a.d + kq;
+    }
+    f32x4_t acc[NACC][MT][NT];
 #pragma unroll
-      for (int u = 0; u < GS; ++u) {
-        const int s = s0 + 4 * u;
-        const int ko = s < nsteps ? s * 32 : 0;
-        av[u] = ld16(mp + ko);
+    for (int q = 0; q < NACC; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[q][mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wave; s0 < nsteps; s0 += NW * GS) {
+      uint4 av[GS][MT], bv[GS][NT];
+#pragma unroll
+      for (int u = 0; u < GS; ++u) {                 // every load of the group first
+        const int s = s0 + NW * u;
+        const int ko = s < nsteps ? s * 32 : 0;      // past the end: a valid address, masked below
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16_stream(mp[mt] + ko);
 #pragma unroll
         for (int t = 0; t < NT; ++t) bv[u][t] = ld16(hp[t] + ko);
       }
 #pragma unroll
       for (int u = 0; u < GS; ++u) {
-        const bool ok = s0 + 4 * u < nsteps;
-        const bf16x8_t A = __builtin_bit_cast(bf16x8_t, ok && mv ? av[u] : z4);
+        if (s0 + NW * u >= nsteps) continue;          // wave-uniform
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          if (!ok) continue;                        // wave-uniform
-          const uint4 b = hv[t] ? bv[u][t] : z4;
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8_t A = __builtin_bit_cast(bf16x8_t, mv[mt] ? av[u][mt] : z4);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint4 bb = hv[t] ? bv[u][t] : z4;
+            acc[u % NACC][mt][t] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, bb), acc[u % NACC][mt][t], 0, 0, 0);
+          }
         }
       }
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4_t v = acc[0][mt][t];
+        if constexpr (NACC == 2) v = v + acc[1][mt][t];
+        if constexpr (NACC == 4) v = (v + acc[1][mt][t]) + (acc[2][mt][t] + acc[3][mt][t]);
+        red[wave][mt * NT + t][lane] = v;
+      }
     __syncthreads();
-    if (wave < NT) {
-      const int t = wave;
-      const f32x4_t v = ((red[0][t][lane] + red[1][t][lane]) + red[2][t][lane]) + red[3][t][lane];
+    if (wave < MT * NT) {                            // wave w finishes tile w
+      const int mt = wave / NT, t = wave % NT;
+      const f32x4_t v = ((red[0][wave][lane] + red[1][wave][lane]) + (red[2][wave][lane] + red[3][wave][lane])) +
+                        ((red[4][wave][lane] + red[5][wave][lane]) + (red[6][wave][lane] + red[7][wave][lane]));
       const int n = n0 + 16 * t + (lane & 15);
-      const int mb = m0 + 4 * (lane >> 4);
+      const int mb = m0 + 16 * mt + 4 * (lane >> 4);
       if (n < a.B) {
         // the four elements m = mb .. mb + 3 (mb % 4 == 0) share one Philox block
         const uint4 wb = a.sample ? rng_block(a.rng, (uint32_t)n, EPI == EPI_KEYS ? 0u : 1u, (uint32_t)mb >> 2)
@@ -243,22 +216,22 @@ __global__ __launch_bounds__(kThreads) void k_mfma(MfmaParams a) {
         }
       }
     }
-    if (EPI == EPI_KEYS && a.mask && blockIdx.y == 0) {
-      for (int j = threadIdx.x; j < 16 * a.W; j += kThreads) {
+    if (EPI == EPI_KEYS && a.mask && blockIdx.y == 0) {   // the selection's per-cluster state, cleared
+      for (int j = threadIdx.x; j < 16 * MT * a.W; j += kMfmaThreads) {
         const int m = m0 + j / a.W;
         if (m < a.rows) a.mask[(size_t)m * a.W + j % a.W] = 0ull;
       }
-      if (threadIdx.x < 16 && m0 + (int)threadIdx.x < a.rows) a.kflag[m0 + threadIdx.x] = 0u;
+      if (threadIdx.x < 16 * MT && m0 + (int)threadIdx.x < a.rows) a.kflag[m0 + threadIdx.x] = 0u;
       if (m0 == 0 && threadIdx.x == 0) *a.nkept = 0;
     }
     __syncthreads();
   }
-  if (EPI == EPI_ARGMAX && wave < NT) {
+  if (EPI == EPI_ARGMAX && wave < MT * NT) {
     uint64_t o = __shfl_xor(bc, 16, kWave);
     bc = o > bc ? o : bc;
     o = __shfl_xor(bc, 32, kWave);
     bc = o > bc ? o : bc;
-    const int n = n0 + 16 * wave + lane;
+    const int n = n0 + 16 * (wave % NT) + lane;
     if (lane < 16 && n < a.B) atomicMax((unsigned long long*)&a.best[(size_t)n * kBestStride], (unsigned long long)bc);
   }
 }
@@ -377,425 +350,6 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const float* keys, int c
     }
   }
   if (tid == 0) best[(size_t)r * kBestStride] = 0ull;
-}
-
-// ------------------------------------------------------------------ B = 1 fused path
-// Three kernels per call.  k_b1_scores streams C (one 4-row group per wave, all row loads
-// issued before any arithmetic) and writes the keys.  k_b1_stage2: every workgroup finds
-// the same kept set from the keys, scores its share of the kept clusters' tiles and writes
-// its best candidate; k_finalize_parts reduces those to the token.  No workgroup ever
-// waits for another.
-
-struct B1Params {
-  const void* h;
-  const char* C;
-  const uint16_t* c_scales;   // int4 centroids: their bf16 group scales
-  int h_bf16, c, d, b, p;
-  int cpad;             // keys padded with NaN up to this count
-  int sample;
-  float tau;
-  Rng rng;
-  float* keys;
-  float* keys_out;      // optional copy of the keys (staged entry point)
-  uint64_t* part;       // [gridDim.x] per-workgroup maxima of k_b1_stage2
-  const int32_t* c2t;
-  const char* tiles;
-  const uint16_t* scales;
-  int32_t* probe_out;
-  float* logits_out;
-  int32_t* tokens_out;
-  int32_t* token;
-};
-
-template <int RF, int CH>
-__global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
-  for (int i = a.c + blockIdx.x * kThreads + threadIdx.x; i < a.cpad; i += gridDim.x * kThreads)
-    a.keys[i] = __uint_as_float(0x7FC00000u);      // quiet NaN padding for k_b1_stage2
-  const int lane = threadIdx.x & 63;
-  const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nw = gridDim.x * 4;
-  const int rb = row_bytes_of(RF, a.d);
-  // h and the first rows are requested together; h is converted once both are in flight
-  HRaw<RF, CH> hraw;
-  load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
-  const int kfirst = wg * kRPI;
-  RowGroup<RF, CH> g;
-  if (kfirst < a.c) rows_load<RF, CH>(g, a.C, rb, kfirst, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
-  HRegs<RF, CH> hr;
-  unpack_h<RF, CH>(hr, hraw, a.h_bf16);
-  for (int k0 = kfirst; k0 < a.c; k0 += nw * kRPI) {
-    if (k0 != kfirst)
-      rows_load<RF, CH>(g, a.C, rb, k0, a.c, RF == RF_INT4 ? a.c_scales : nullptr, a.d >> 7, lane);
-    float s[kRPI];
-    rows_dot<RF, CH>(g, hr, s);
-    {                                            // lane i < kRPI: the key of row k0 + i
-      const float si = lane_pick<kRPI>(s, lane);
-      const int k = k0 + lane;
-      if (lane < kRPI && k < a.c) {
-        const float key = make_key(si, a.sample, a.tau, a.rng, 0u, 0u, (uint32_t)k);
-        a.keys[k] = key;
-        if (a.keys_out) a.keys_out[k] = key;
-      }
-    }
-  }
-}
-
-
-// Shared state of k_b1_stage2.  Keys live in registers: slot s of thread t holds the key of
-// cluster s * 1024 + t, so one wave ballot covers 64 consecutive clusters and the kept set
-// is written as 64-bit words without atomics.
-// Key slots per thread of k_b1_stage2: the power of two >= c / 1024 (at least 2).  At B = 1
-// the workspace keys are padded to kB1Threads * slots with quiet NaNs, which every min, max
-// and comparison of the selection ignores.
-__host__ __device__ __forceinline__ int b1_key_slots(int c) {
-  int s = 2;
-  while (s * kB1Threads < c) s *= 2;
-  return s;
-}
-
-constexpr int kS2MaxWords = 32768 / 64;
-constexpr int kS2MaxCand = 64;             // keys the boundary bin may hold on the fast path
-
-struct S2Shared {
-  int hist[kSelBins];
-  // Bitmaps over the clusters, wave-major: bit l of w[wave NS + s] is cluster s 1024 + 64 wave + l.
-  uint64_t words[kS2MaxWords];             // clusters certainly kept (or all kept, general path)
-  uint64_t fullw[kS2MaxWords];             // all kept clusters (probe outputs only)
-  int pref[kS2MaxWords];                   // kept clusters before id-ordered word i (probe ids)
-  float wmx[16], wmn[16];
-  int wtot[16];
-  int bnd[3];                              // boundary bin, keys above it, keys in it
-  int ncand;
-  float cx[kS2MaxCand];                    // the boundary bin's keys ...
-  int cid[kS2MaxCand];                     // ... and clusters
-  int bk[kS2MaxCand];                      // boundary clusters that are kept, ascending id
-  uint64_t wmax[16];
-};
-
-// Position of id-ordered word iw in a wave-major bitmap with NS slots.
-template <int NS>
-__device__ __forceinline__ int wm_index(int iw) { return (iw & 15) * NS + (iw >> 4); }
-
-// Cluster id of ascending rank q (wave-uniform) among the set bits of a wave-major bitmap;
-// lane l scans the id-ordered words [l WPL, l WPL + WPL).
-template <int NS>
-__device__ __forceinline__ int kept_rank_id(const uint64_t* words, int q) {
-  constexpr int NW = NS * 16, WPL = NW >= 64 ? NW / 64 : 1;
-  const int lane = threadIdx.x & 63;
-  uint64_t wv[WPL];
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < WPL; ++i) {
-    const int iw = lane * WPL + i;
-    wv[i] = iw < NW ? words[wm_index<NS>(iw)] : 0ull;
-    cnt += __popcll(wv[i]);
-  }
-  const int incl = wave_incl_scan(cnt);
-  const uint64_t hit = __ballot(incl > q);
-  const int L = __ffsll((unsigned long long)hit) - 1;
-  int id = 0;
-  if (lane == L) {
-    int r = q - (incl - cnt);
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      const int pc = __popcll(wv[i]);
-      if (r >= 0 && r < pc) {
-        uint64_t bits = wv[i];
-        for (int k = 0; k < r; ++k) bits &= bits - 1ull;
-        id = (lane * WPL + i) * 64 + __ffsll((unsigned long long)bits) - 1;
-      }
-      r -= pc;
-    }
-  }
-  return __builtin_amdgcn_readlane(id, L);
-}
-
-// Set bits below cluster k (wave-uniform) in a wave-major bitmap: the ascending rank of k.
-template <int NS>
-__device__ __forceinline__ int kept_count_below(const uint64_t* words, int k) {
-  constexpr int NW = NS * 16, WPL = NW >= 64 ? NW / 64 : 1;
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < WPL; ++i) {
-    const int iw = lane * WPL + i;
-    if (iw < NW && iw <= (k >> 6)) {
-      const uint64_t w = words[wm_index<NS>(iw)];
-      cnt += __popcll(iw < (k >> 6) ? w : (w & ((1ull << (k & 63)) - 1ull)));
-    }
-  }
-  return __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
-}
-
-// Selection and stage 2 for one row in one kernel.  Every workgroup (1024 threads, one per
-// CU) reads the c keys and finds the same kept set, so no workgroup waits for another:
-//  * one float-linear 2048-bin histogram between the key min and max locates the bin b
-//    holding the p-th largest key; every key in a bin above b is certainly kept;
-//  * the clusters are numbered 0 .. p-1 in this order: the certain ones by ascending id,
-//    then the kept keys of bin b by ascending id; workgroup g takes the numbers g, g + G, ..;
-//  * the certain clusters are resolved and their tile loads issued while wave 0 ranks the
-//    keys of bin b exactly (key desc, id asc) to pick the p - above of them that are kept.
-// A boundary bin with more than kS2MaxCand keys (or all keys equal) sends the workgroup to
-// the general selection (select_regs), after which every cluster is resolved from the full
-// kept bitmap.  Each workgroup writes the packed maximum of its tokens to part[g];
-// k_finalize_parts turns the maxima into the token.  Probe outputs are indexed by the
-// ascending rank of the cluster among all kept ones.  NS: key slots per thread, NR: tile rows
-// per wave step.
-template <int RF, int CH, int NS, int NR>
-__global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
-  constexpr int NT = kB1Threads, NWAVE = NT / 64;
-  constexpr int KV = NS >= 4 ? NS / 4 : 1;             // uint4 per thread of the general selection
-  constexpr int NWID = NS * 16;                        // 64-bit bitmap words, padding included
-  constexpr bool kEarlyH = CH * Fmt<RF>::EPC <= 32;    // h loads issued with the first tile rows
-  __shared__ __align__(16) S2Shared Q;
-  __shared__ SelShared S;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = gridDim.x, me = blockIdx.x;
-  const int c = a.c, p = a.p;
-  const bool want = a.probe_out || a.logits_out || a.tokens_out;
-  // ---- keys; the slots past c hold NaN: ignored by min / max, never greater or equal
-  float x[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) x[s] = a.keys[s * NT + tid];
-  for (int i = tid; i < kSelBins; i += NT) Q.hist[i] = 0;
-  if (tid == 0) Q.ncand = 0;
-  float mx = x[0], mn = x[0];
-#pragma unroll
-  for (int s = 1; s < NS; ++s) { mx = fmaxf(mx, x[s]); mn = fminf(mn, x[s]); }
-  mx = wave_minmax_f32<true>(mx);
-  mn = wave_minmax_f32<false>(mn);
-  if (lane == 0) { Q.wmx[wave] = mx; Q.wmn[wave] = mn; }
-  __syncthreads();                                                          // 1
-  float hi = Q.wmx[0], lo = Q.wmn[0];
-#pragma unroll
-  for (int w = 1; w < NWAVE; ++w) { hi = fmaxf(hi, Q.wmx[w]); lo = fminf(lo, Q.wmn[w]); }
-  const float inv = (float)kSelBins / (hi - lo);
-  bool fast = hi > lo && inv > 0.f && inv < 3.0e38f;                        // block-uniform
-  const float off = -lo * inv;
-  int bins[NS];
-  if (fast) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {                 // NaN padding lands in bin 0
-      bins[s] = (int)fminf(fmaxf(fmaf(x[s], inv, off), 0.f), (float)(kSelBins - 1));
-      atomicAdd(&Q.hist[bins[s]], 1);
-    }
-    if (tid == 0 && NS * NT > c) atomicSub(&Q.hist[0], NS * NT - c);
-  }
-  __syncthreads();                                                          // 2
-  // ---- boundary bin: wave w scans bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
-  const int top = kSelBins - 1 - 128 * wave - 2 * lane;
-  int h_lo = 0, h_hi = 0, incl = 0;
-  if (fast) {
-    const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
-    h_lo = hh.x;
-    h_hi = hh.y;
-    incl = wave_incl_scan(h_lo + h_hi);
-    if (lane == 63) Q.wtot[wave] = incl;
-  }
-  __syncthreads();                                                          // 3
-  if (fast) {
-    int before = 0, bw = -1;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const int t = Q.wtot[w];
-      if (bw < 0) {
-        if (before + t >= p) bw = w;
-        else before += t;
-      }
-    }
-    if (wave == bw) {                       // the slice holding the p-th key resolves it
-      const int cum = incl + before;
-      const int L = __ffsll((unsigned long long)__ballot(cum >= p)) - 1;
-      const int ex = cum - h_lo - h_hi;
-      if (lane == L) {
-        const bool upper = ex + h_hi >= p;
-        Q.bnd[0] = upper ? top : top - 1;
-        Q.bnd[1] = upper ? ex : ex + h_hi;
-        Q.bnd[2] = upper ? h_hi : h_lo;
-      }
-    }
-  }
-  __syncthreads();                                                          // 4
-  int b = 0, above = 0, inb = 0;
-  if (fast) {
-    b = Q.bnd[0];
-    above = Q.bnd[1];
-    inb = Q.bnd[2];
-    fast = b > 0 && inb <= kS2MaxCand;
-  }
-  // ---- the certain clusters (bins above b) as a bitmap; the keys of bin b compacted
-  if (fast) {
-    uint32_t wlo = 0u, whi = 0u;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint64_t m = __ballot(bins[s] > b);
-      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
-      put_lane(whi, (uint32_t)(m >> 32), s);
-      const uint64_t e = __ballot(bins[s] == b);
-      if (e) {
-        int base = 0;
-        if (lane == __ffsll((unsigned long long)e) - 1) base = atomicAdd(&Q.ncand, __popcll(e));
-        base = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(base, __ffsll((unsigned long long)e) - 1));
-        const int pos = base + lane_prefix(e);
-        if (bins[s] == b && pos < kS2MaxCand) { Q.cx[pos] = x[s]; Q.cid[pos] = s * NT + tid; }
-      }
-    }
-    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-  }
-  __syncthreads();                                                          // 5
-  if (fast) fast = Q.ncand == inb;          // block-uniform
-  int n_def = above;                        // numbers below n_def index Q.words
-  if (!fast) {                              // the general selection, then the full kept bitmap
-    uint32_t u[KV][4];
-    uint32_t Tu;
-    int Tid;
-    load_keys<KV>(a.keys, c, u, S);
-    select_regs<KV>(u, c, p, S, Tu, Tid);
-    const float T = ord_to_float(Tu);
-    uint32_t wlo = 0u, whi = 0u;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float v = a.keys[s * NT + tid];
-      const uint64_t m = __ballot(v > T) | __ballot(v == T && s * NT + tid <= Tid);
-      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
-      put_lane(whi, (uint32_t)(m >> 32), s);
-    }
-    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-    n_def = p;
-  }
-  const int n_my = me < p ? (p - me + G - 1) / G : 0;
-  const int gpp = (a.b + NR - 1) / NR;
-  const int nit = n_my * gpp;
-  const int rb = row_bytes_of(RF, a.d);
-  const int spr = a.d >> 7;
-  // this wave's first tile rows, when certain: resolved and loaded while wave 0 ranks
-  RowGroup<RF, CH, NR> g0;
-  int tl0 = 0, k0 = -1;
-  HRaw<RF, CH> hraw;
-  if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
-  if (fast) {
-    if (wave == 0) {                        // rank the boundary keys; keep the first p - above
-      const int n = inb;
-      const int need = p - above;
-      const bool act = lane < n;
-      const float xt = act ? Q.cx[lane] : 0.f;
-      const int it = act ? Q.cid[lane] : 0x7FFFFFFF;
-      int rank = 0;
-      for (int q = 0; q < n; ++q) {
-        const float xq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), q));
-        const int iq = __builtin_amdgcn_readlane(it, q);
-        rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
-      }
-      const bool kept = act && rank < need;
-      int pos = 0;
-      for (int q = 0; q < n; ++q) {
-        const int rq = __builtin_amdgcn_readlane(rank, q);
-        const int iq = __builtin_amdgcn_readlane(it, q);
-        pos += (rq < need && iq < it) ? 1 : 0;
-      }
-      if (kept) Q.bk[pos] = it;
-    }
-    if (wave < nit) {
-      const int qi = wave / gpp, j0 = (wave - qi * gpp) * NR;
-      const int q = me + qi * G;
-      if (q < above) {
-        k0 = kept_rank_id<NS>(Q.words, q);
-        const size_t row0 = (size_t)k0 * a.b;
-        tl0 = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
-        rows_load<RF, CH>(g0, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
-                          spr, lane);
-      }
-    }
-  }
-  __syncthreads();                                                          // 6
-  // ---- probe outputs: the full kept bitmap gives every cluster its ascending rank
-  const uint64_t* fw = fast ? Q.fullw : Q.words;
-  if (want) {
-    if (fast) {
-      for (int i = tid; i < NWID; i += NT) Q.fullw[i] = Q.words[i];
-      __syncthreads();
-      if (tid < p - above) {
-        const int k = Q.bk[tid];
-        atomicOr((unsigned long long*)&Q.fullw[(((k >> 6) & 15) * NS) + (k >> 10)], 1ull << (k & 63));
-      }
-      __syncthreads();
-    }
-    if (me == 0 && a.probe_out) {
-      int tot;
-      const int pc = tid < NWID ? __popcll(fw[wm_index<NS>(tid)]) : 0;
-      const int ex = block_scan(pc, Q.wtot, tot);
-      if (tid < NWID) Q.pref[tid] = ex;
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint64_t m = fw[wave * NS + s];
-        if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
-      }
-    }
-  }
-  // ---- stage 2 on this workgroup's clusters
-  HRegs<RF, CH> hr;
-  if constexpr (kEarlyH) unpack_h<RF, CH>(hr, hraw, a.h_bf16);
-  else load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
-  uint64_t bc = 0;
-  for (int it = wave; it < nit; it += NWAVE) {
-    const int qi = it / gpp, j0 = (it - qi * gpp) * NR;
-    const int q = me + qi * G;
-    int k, tl;
-    RowGroup<RF, CH, NR> g;
-    if (it == wave && k0 >= 0) {
-      k = k0;
-      tl = tl0;
-      g = g0;
-    } else {
-      k = q < n_def ? kept_rank_id<NS>(Q.words, q) : Q.bk[q - n_def];
-      const size_t row0 = (size_t)k * a.b;
-      tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
-      rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
-                        spr, lane);
-    }
-    float z[NR];
-    rows_dot<RF, CH>(g, hr, z);
-    const int qo = want ? kept_count_below<NS>(fw, k) : 0;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int j = j0 + i;
-      if (j < a.b) {
-        const int t = __builtin_amdgcn_readlane(tl, i);
-        const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
-        const uint64_t cnd = pack_cand(key, (uint32_t)t);
-        bc = cnd > bc ? cnd : bc;
-        if (want && lane == 0) {
-          if (a.logits_out) a.logits_out[(size_t)qo * a.b + j] = z[i];
-          if (a.tokens_out) a.tokens_out[(size_t)qo * a.b + j] = t;
-        }
-      }
-    }
-  }
-  if (lane == 0) Q.wmax[wave] = bc;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t m = Q.wmax[0];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) m = Q.wmax[w] > m ? Q.wmax[w] : m;
-    a.part[me] = m;
-  }
-}
-
-// The token of the fused B = 1 path: the largest of the per-workgroup maxima part[0 .. n).
-__global__ __launch_bounds__(256) void k_finalize_parts(const uint64_t* part, int n, int32_t* token) {
-  __shared__ uint64_t wm[4];
-  const int tid = threadIdx.x;
-  uint64_t m = 0;
-  for (int i = tid; i < n; i += 256) m = part[i] > m ? part[i] : m;
-  m = wave_max_u64(m);
-  if ((tid & 63) == 0) wm[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t r = wm[0];
-    for (int w = 1; w < 4; ++w) r = wm[w] > r ? wm[w] : r;
-    token[0] = (int32_t)cand_id(r);
-  }
 }
 
 // ------------------------------------------------------------------ stage 2
@@ -968,6 +522,7 @@ __global__ void k_fill_u64(uint64_t* p, int n, uint64_t v) {
 struct DenseParams {
   const void* h;
   const char* E;
+  const uint16_t* scales;     // int4 rows: their bf16 group scales [V][d/128]
   int h_bf16, B, V, d;
   int sample;
   float tau;
@@ -989,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void k_dense_gemv(DenseParams a) {
   uint64_t bc = 0;
   for (int t0 = wg * kRPI; t0 < a.V; t0 += nw * kRPI) {
     RowGroup<RF, CH> g;
-    rows_load<RF, CH>(g, a.E, rb, t0, a.V, nullptr, 0, lane);
+    rows_load<RF, CH>(g, a.E, rb, t0, a.V, RF == RF_INT4 ? a.scales : nullptr, a.d >> 7, lane);
     float z[kRPI];
     rows_dot<RF, CH>(g, hr, z);
     {                                            // lane i < kRPI: the token t0 + i
@@ -1180,7 +735,8 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   size_t off = 0;
   char* b = (char*)base;
   w.keys = (float*)(b ? b + off : nullptr);
-  off = up(off + (B == 1 ? (size_t)b1_key_slots(c) * kB1Threads : (size_t)B * c) * sizeof(float));
+  off = up(off + (B == 1 ? (size_t)b1_key_slots(c) : (size_t)B * c) * sizeof(float));
+
   w.mask = nullptr;
   w.kflag = nullptr;
   w.klist = nullptr;
@@ -1236,47 +792,20 @@ int chunk_slots(int fmt, int d) {
     default: return hipErrorInvalidValue;                         \
   }
 
-template <int RF, int CH>
-static void launch_b1_scores(const B1Params& a, int c, hipStream_t st) {
-  const int groups = (c + kRPI - 1) / kRPI;          // one row group per wave
-  const int wgs = (groups + 3) / 4;
-  hipLaunchKernelGGL((k_b1_scores<RF, CH>), dim3(wgs), dim3(kThreads), 0, st, a);
-}
-
-template <int RF, int CH, int S>
-static void launch_b1_stage2_s(const B1Params& a, int G, int nr, hipStream_t st) {
-  if (nr == 1) hipLaunchKernelGGL((k_b1_stage2<RF, CH, S, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
-  else         hipLaunchKernelGGL((k_b1_stage2<RF, CH, S, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
-}
-
-template <int RF, int CH>
-static void launch_b1_stage2(const B1Params& a, int c, int p, int b, hipStream_t st) {
-  const int G = p < kB1Workgroups ? p : kB1Workgroups;
-  const int n_my = (p + G - 1) / G;
-  const int nr = n_my * b <= kB1Threads / 64 ? 1 : 2;     // one row per wave when that fills them
-  const int slots = (c + kB1Threads - 1) / kB1Threads;
-  if (slots <= 2)       launch_b1_stage2_s<RF, CH, 2>(a, G, nr, st);
-  else if (slots <= 4)  launch_b1_stage2_s<RF, CH, 4>(a, G, nr, st);
-  else if (slots <= 8)  launch_b1_stage2_s<RF, CH, 8>(a, G, nr, st);
-  else if (slots <= 16) launch_b1_stage2_s<RF, CH, 16>(a, G, nr, st);
-  else                  launch_b1_stage2_s<RF, CH, 32>(a, G, nr, st);
-  hipLaunchKernelGGL(k_finalize_parts, dim3(1), dim3(256), 0, st, (const uint64_t*)a.part, G, a.token);
-}
-
 static bool use_mfma(const HeadShape& s, int fmt) {
   return s.B > 1 && s.h_bf16 && fmt == RF_BF16 && (s.d % 32) == 0;
 }
 
 template <int NT, int EPI>
 static void launch_mfma_nt(const MfmaParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_mfma<NT, EPI>), grid, dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((k_mfma<NT, EPI>), grid, dim3(kMfmaThreads), 0, st, p);
 }
 
 template <int EPI>
 static hipError_t launch_mfma(const MfmaParams& p, int max_wg, hipStream_t st) {
-  const int ntiles = (p.rows + 15) / 16;
+  const int ngroups = (p.rows + 16 * kMfmaMT - 1) / (16 * kMfmaMT);
   const int nb = (p.B + 63) / 64;
-  dim3 grid(ntiles < max_wg ? ntiles : max_wg, nb);
+  dim3 grid(ngroups < max_wg ? ngroups : max_wg, nb);
   const int nt = p.B >= 64 ? 4 : (p.B + 15) / 16;
   switch (nt) {
     case 1: launch_mfma_nt<1, EPI>(p, grid, st); break;
@@ -1293,19 +822,12 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
   const uint16_t* c_scales =
       s.c_fmt == RF_INT4 ? (const uint16_t*)((const char*)C + int4_scales_offset(s.c, s.d)) : nullptr;
   if (s.B == 1) {   // the same kernel the fused B = 1 forward runs
-    B1Params a{};
-    a.h = h; a.C = (const char*)C; a.c_scales = c_scales; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d;
-    a.sample = smp.sample; a.tau = smp.tau; a.rng = rng;
-    a.keys = ws.keys; a.keys_out = keys_out; a.cpad = b1_key_slots(s.c) * kB1Threads;
-    const int ch = chunk_slots(s.c_fmt, s.d);
-    if (s.c_fmt == RF_F32) {
-      FH_DISPATCH_CH(ch, (launch_b1_scores<RF_F32, kCH>(a, s.c, st)));
-    } else if (s.c_fmt == RF_BF16) {
-      FH_DISPATCH_CH(ch, (launch_b1_scores<RF_BF16, kCH>(a, s.c, st)));
-    } else {
-      FH_DISPATCH_CH_INT4(ch, (launch_b1_scores<RF_INT4, kCH>(a, s.c, st)));
-    }
-    return hipGetLastError();
+    B1Args a{};
+    a.h = h; a.C = C; a.c_scales = c_scales; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b;
+    a.sample = smp.sample; a.tau = smp.tau; a.seed = smp.seed; a.step = smp.step;
+    a.keys = ws.keys; a.keys_out = keys_out;
+    return s.c_fmt == RF_F32 ? launch_b1_scores_f32(a, st)
+         : s.c_fmt == RF_BF16 ? launch_b1_scores_bf16(a, st) : launch_b1_scores_int4(a, st);
   }
   if (use_mfma(s, s.c_fmt)) {
     MfmaParams p{};
@@ -1379,21 +901,14 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
 hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int32_t* c2t, const void* tiles,
                             const uint16_t* scales, const Sampling& smp, const Workspace& ws, int32_t* probe_out,
                             float* logits_out, int32_t* tokens_out, int32_t* token, hipStream_t st) {
-  B1Params a{};
+  B1Args a{};
   a.h = h; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
-  a.sample = smp.sample; a.tau = smp.tau; a.rng = make_rng(smp.seed, smp.step);
+  a.sample = smp.sample; a.tau = smp.tau; a.seed = smp.seed; a.step = smp.step;
   a.keys = ws.keys; a.part = ws.part;
-  a.c2t = c2t; a.tiles = (const char*)tiles; a.scales = scales;
+  a.c2t = c2t; a.tiles = tiles; a.scales = scales;
   a.probe_out = probe_out; a.logits_out = logits_out; a.tokens_out = tokens_out; a.token = token;
-  const int ch = chunk_slots(s.e_fmt, s.d);
-  if (s.e_fmt == RF_F32) {
-    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_F32, kCH>(a, s.c, p, s.b, st)));
-  } else if (s.e_fmt == RF_BF16) {
-    FH_DISPATCH_CH(ch, (launch_b1_stage2<RF_BF16, kCH>(a, s.c, p, s.b, st)));
-  } else {
-    FH_DISPATCH_CH_INT4(ch, (launch_b1_stage2<RF_INT4, kCH>(a, s.c, p, s.b, st)));
-  }
-  return hipGetLastError();
+  return s.e_fmt == RF_F32 ? launch_b1_stage2_f32(a, st)
+       : s.e_fmt == RF_BF16 ? launch_b1_stage2_bf16(a, st) : launch_b1_stage2_int4(a, st);
 }
 
 hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E, const Sampling& smp,
@@ -1411,7 +926,9 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
     p.best = best; p.logits = logits;
     e = launch_mfma<EPI_ARGMAX>(p, 2048, st);
   } else {
-    DenseParams a{h, (const char*)E, s.h_bf16, s.B, V, s.d, smp.sample, smp.tau, rng, best, logits};
+    const uint16_t* sc =
+        s.e_fmt == RF_INT4 ? (const uint16_t*)((const char*)E + int4_scales_offset((size_t)V, (size_t)s.d)) : nullptr;
+    DenseParams a{h, (const char*)E, sc, s.h_bf16, s.B, V, s.d, smp.sample, smp.tau, rng, best, logits};
     const int groups = (V + kRPI - 1) / kRPI;
     int wgs = (groups + 3) / 4;
     if (wgs > 2048) wgs = 2048;
@@ -1419,8 +936,10 @@ hipError_t launch_dense(const HeadShape& s, int V, const void* h, const void* E,
     const int ch = chunk_slots(s.e_fmt, s.d);
     if (s.e_fmt == RF_F32) {
       FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_dense_gemv<RF_F32, kCH>), grid, dim3(kThreads), 0, st, a));
-    } else {
+    } else if (s.e_fmt == RF_BF16) {
       FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_dense_gemv<RF_BF16, kCH>), grid, dim3(kThreads), 0, st, a));
+    } else {
+      FH_DISPATCH_CH_INT4(ch, hipLaunchKernelGGL((k_dense_gemv<RF_INT4, kCH>), grid, dim3(kThreads), 0, st, a));
     }
     e = hipGetLastError();
   }

@@ -77,6 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_mc_marginal": ([D, vp, vp, vp, vp, vp, i64, f32, u64, i64, i32, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_dense_workspace_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_dense_forward": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp, vp], ctypes.c_int),
+        "flashhead_philox_words": ([u64, ctypes.c_uint32, u64, ctypes.c_uint32, ctypes.c_uint32, i64, vp, vp, vp],
+                                   ctypes.c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -245,3 +247,9 @@ def flashhead_mc_marginal(desc: fh_desc, h, centroids, cluster_tokens, E_tiles, 
         ctypes.byref(desc), _ptr(h), _ptr(centroids), _ptr(cluster_tokens), _ptr(E_tiles), _ptr(E_scales), int(p),
         float(temperature), int(seed), int(n_sets), int(bool(clip)), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+
+
+def flashhead_philox_words(seed, row, step, rng_stream, n0, count, words_out=None, gumbel_out=None,
+                           stream=None) -> None:
+    _check(load_library().flashhead_philox_words(int(seed), int(row), int(step), int(rng_stream), int(n0),
+                                                 int(count), _ptr(words_out), _ptr(gumbel_out), _stream(stream)))

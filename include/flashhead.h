@@ -197,8 +197,8 @@ fh_status flashhead_centroid_scores(const fh_desc* desc, const void* h, const vo
  * clusters drawn without replacement from softmax(s / tau).  Reads the keys the last
  * flashhead_centroid_scores call left in `workspace`; writes the kept ids, ascending, to
  * the workspace and, if probe_ids_out (device, int32 [B][p]) is non-NULL, there too.  At
- * B > 1 the selection also records, per cluster, the rows that kept it; that state is
- * cleared by flashhead_centroid_scores, so each selection needs its own stage-1 call.
+ * B > 1 the selection also records, per cluster, the rows that kept it (cleared first by
+ * this call, so selections may follow each other on one workspace with any p).
  */
 fh_status flashhead_select_probes(const fh_desc* desc, int64_t p, void* workspace,
                                   size_t workspace_bytes, int32_t* probe_ids_out, void* stream);
@@ -290,7 +290,11 @@ fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes);
  * The dense head the paper starts from (Section 3): z = E h over all V tokens, then argmax
  * (greedy) or argmax z / tau + G(U(seed, r, step, 1, t)) (sampling), ties to the smaller id.
  * The same token keys as flashhead_forward's stage 2, so p = c gives identical tokens.
- *   E       device [V][d] token-major, desc->e_dtype F32 | BF16
+ *   E       device [V][d] token-major, desc->e_dtype F32 | BF16 | INT4_G128; INT4_G128 is one
+ *           buffer: the nibbles [V][d/2] (the tile format of flashhead_pack), then from byte
+ *           round_up(V d / 2, 256) the bf16 group scales [V][d/128] -- the layout
+ *           flashhead_centroids writes, so a c = V, b = 1 call with C2T[t][0] = t quantises E
+ *           (the dense head of the paper's quantisation comparison, Section 4.5, Table 5)
  *   token   device int32 [B] out
  *   logits  device float [B][V] out, may be NULL
  */
@@ -298,6 +302,19 @@ fh_status flashhead_dense_forward(const fh_desc* desc, const void* h, const void
                                   int32_t mode, float temperature, uint64_t seed, uint64_t step,
                                   void* workspace, size_t workspace_bytes, int32_t* token,
                                   float* logits, void* stream);
+
+/*
+ * The sampler's random numbers exactly as the kernels draw them (the Philox4x32-10 counter
+ * layout above; Section 3.2 samples clusters and tokens but fixes no generator), for checking
+ * the generator against another implementation:
+ *   words_out[i]  = the Philox word of element n = n0 + i of (seed, row, step, rng_stream)
+ *   gumbel_out[i] = G(u) = -ln(-ln u) in fp32 (logf), u = (2 (word >> 9) + 1) 2^-24
+ * Either output may be NULL (not both); both are device arrays of `count` elements.
+ * rng_stream 0 .. 3; count >= 0 with n0 + count <= 2^32, else FH_ERR_ARG.
+ */
+fh_status flashhead_philox_words(uint64_t seed, uint32_t row, uint64_t step, uint32_t rng_stream,
+                                 uint32_t n0, int64_t count, uint32_t* words_out, float* gumbel_out,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

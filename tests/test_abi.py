@@ -124,8 +124,11 @@ def test_stage_and_dense_argument_checks(lib):
     assert L.flashhead_probe_logits(ctypes.byref(d), 8, FAKE, FAKE, FAKE, None, 0, 1.0, 0, 0, FAKE, 1 << 30,
                                     ctypes.byref(out), None) == fh.FH_ERR_ARG
     d4 = fh.make_desc(1, 3072, 128256, 8016, e_dtype="int4")
-    assert L.flashhead_dense_forward(ctypes.byref(d4), FAKE, FAKE, 0, 1.0, 0, 0, FAKE, 1 << 20, FAKE, None, None) \
-        == fh.FH_ERR_DTYPE
+    d4s = fh.make_desc(1, 3080, 128256, 8016, e_dtype="int4")        # int4 rows need d % 128 == 0
+    assert L.flashhead_dense_forward(ctypes.byref(d4s), FAKE, FAKE, 0, 1.0, 0, 0, FAKE, 1 << 20, FAKE, None, None) \
+        == fh.FH_ERR_SHAPE
+    assert L.flashhead_dense_forward(ctypes.byref(d4), FAKE, None, 0, 1.0, 0, 0, FAKE, 1 << 20, FAKE, None, None) \
+        == fh.FH_ERR_ARG
     assert L.flashhead_dense_forward(ctypes.byref(d), FAKE, FAKE, 0, 1.0, 0, 0, FAKE, 0, FAKE, None, None) \
         == fh.FH_ERR_WORKSPACE
     assert L.flashhead_pack(ctypes.byref(d), 2, FAKE, FAKE, FAKE, None, None) == fh.FH_ERR_DTYPE
@@ -163,3 +166,12 @@ def test_mc_marginal_argument_checks(lib):
     assert _mc(d, ws_bytes=need - 1) == fh.FH_ERR_WORKSPACE
     d4 = fh.make_desc(1, 3072, 128256, 8016, e_dtype="int4")
     assert _mc(d4, scales=None) == fh.FH_ERR_ARG
+
+
+def test_philox_words_argument_checks(lib):
+    L = fh.load_library()
+    assert L.flashhead_philox_words(1, 0, 0, 4, 0, 16, FAKE, None, None) == fh.FH_ERR_ARG       # stream 0..3
+    assert L.flashhead_philox_words(1, 0, 0, 0, 0, -1, FAKE, None, None) == fh.FH_ERR_ARG       # count < 0
+    assert L.flashhead_philox_words(1, 0, 0, 0, 0xFFFFFFFF, 2, FAKE, None, None) == fh.FH_ERR_ARG   # n past 2^32
+    assert L.flashhead_philox_words(1, 0, 0, 0, 0, 16, None, None, None) == fh.FH_ERR_ARG      # no output
+    assert L.flashhead_philox_words(1, 0, 0, 0, 5, 0, FAKE, None, None) == fh.FH_OK            # nothing to do

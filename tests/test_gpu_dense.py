@@ -16,6 +16,7 @@ import torch
 import workloads
 from clustered_retrieval_lm_amd import flashhead as fh
 from clustered_retrieval_lm_amd.head import to_device
+from oracle import codecs
 from oracle import head as ohead
 from oracle import philox
 
@@ -30,6 +31,9 @@ CASES = [
     (256, 5000, 3, "bf16"),      # B > 1 below the MFMA batch tile
     (256, 5000, 70, "bf16"),     # MFMA path, ragged batch
     (96, 2000, 5, "f32"),
+    # int4-g128 token rows (the quantised dense head of the paper's Table 5 comparison)
+    (256, 3000, 1, "int4"),
+    (1152, 2000, 3, "int4"),     # 9 groups per row, ragged chunk slots
 ]
 
 
@@ -37,19 +41,26 @@ CASES = [
 @pytest.mark.parametrize("mode", ["greedy", "sample"])
 def test_dense_head_matches_the_oracle(gpu, d, V, B, dt, mode):
     rng = np.random.default_rng(d + V + B)
-    E = workloads.to_storage(rng.standard_normal((V, d)), dt)
-    h = workloads.to_storage(rng.standard_normal((B, d)), dt)
+    hdt = "bf16" if dt == "int4" else dt
+    h = workloads.to_storage(rng.standard_normal((B, d)), hdt)
+    if dt == "int4":
+        # rows quantised from bf16 values; the library takes nibbles then scales in one buffer
+        Eo = codecs.int4_quantize(codecs.bf16_to_f64(workloads.to_storage(rng.standard_normal((V, d)), "bf16")))
+        Ed = to_device(H.centroid_buffer(Eo, "int4"), gpu)
+    else:
+        Eo = workloads.to_storage(rng.standard_normal((V, d)), dt)
+        Ed = to_device(Eo, gpu)
     tau, seed, step = 0.8, 9, 3
-    desc = fh.make_desc(B, d, V, 1, dt, dt, dt)
+    desc = fh.make_desc(B, d, V, 1, hdt, hdt, dt)
     ws = torch.empty(fh.flashhead_dense_workspace_bytes(desc), dtype=torch.uint8, device=gpu)
     tok = torch.empty(B, dtype=torch.int32, device=gpu)
     logits = torch.empty(B, V, dtype=torch.float32, device=gpu)
-    fh.flashhead_dense_forward(desc, to_device(h, gpu), to_device(E, gpu), mode, tau, seed, step, ws, tok, logits)
+    fh.flashhead_dense_forward(desc, to_device(h, gpu), Ed, mode, tau, seed, step, ws, tok, logits)
     torch.cuda.synchronize()
     got_z = logits.cpu().numpy().astype(np.float64)
     got_t = tok.cpu().numpy()
-    ref = ohead.dense_forward(h, dt, E, dt, mode=mode, tau=tau, seed=seed, step=step)
-    L = H.L_mfma(d) if (B > 1 and dt == "bf16" and d % 32 == 0) else H.L_gemv(dt, d)
+    ref = ohead.dense_forward(h, hdt, Eo, dt, mode=mode, tau=tau, seed=seed, step=step)
+    L = H.L_mfma(d, B) if (B > 1 and dt == "bf16" and d % 32 == 0) else H.L_gemv(dt, d)
     dz = np.abs(got_z - ref.z)
     assert np.all(dz <= H.gamma(L) * ref.absz + 1e-30), "logit error beyond the rounding bound"
     if dt == "f32":
