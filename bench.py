@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """FlashHead head throughput on one MI355X.
 
-Workload (default): the Gemma-3-1B head shape of the FlashHead paper's experiments
-(Section 4, Table 4): B = 1, d = 1152, V = 262144 tokens in c = 16384 balanced clusters of 16,
-p = 512 probes, bf16 centroids / tiles / hidden state, greedy decoding.  Inputs are the seeded
-synthetic head of workloads.py with the stored balanced clustering of that head
+Headline workload: the Gemma-3-1B head shape of the FlashHead paper's experiments (Section 4,
+Table 4): B = 1, d = 1152, V = 262144 tokens in c = 16384 balanced clusters of 16, p = 512
+probes, bf16 centroids / tiles / hidden state, greedy decoding.  Inputs are the seeded synthetic
+head of workloads.py with the stored balanced clustering of that head
 (tests/golden/clusters_gemma.npz); centroids and tiles are built on the GPU by the library.
 
 A step is one flashhead_forward call (centroid scores, probe selection, probe logits, token)
-over one hidden state.  Calls are captured in a HIP graph that cycles through R copies of the
-centroids and R distinct hidden states over the one tile array, as a decode loop does: every
-call reads the centroids from HBM (R x 37.7 MB is well above the 256 MB last-level cache) and
-its own probe set's tiles (R different probe sets touch ~R x 19 MB of the 604 MB tiles).
-Prints one JSON line.
+over one batch of hidden states.  Calls are captured in HIP graphs that cycle through R copies
+of the centroids, R copies of the tile array and R distinct hidden states, as a decode loop
+does: every call reads its centroids and its probe set's tiles from HBM (R x the bytes of a
+call is well above twice the 256 MB last-level cache).  The timed region is exactly --steps
+calls after exactly --warmup untimed calls.
+
+The same line carries every other workload (Llama-3.2-1B shape, Gemma sampling, int4
+centroids, the Qwen-3 batched head greedy and sampling, int4 tiles at B = 1 and 16) under
+"configs", each with the on-GPU dense head as comparator, and the oracle timed on the host
+cores with one thread and with all of them.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma] [--mode greedy]
        python bench.py --sweep      (clusters x probes grid at the Llama-3.2-1B head shape)
@@ -20,6 +25,7 @@ usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma] [-
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -29,21 +35,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
+CONFIG_CALLS = 200          # calls per graph of a secondary configuration
+CONFIG_REPLAYS = 5
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, B=1):
-    """Bytes a call must read at least: centroids, the kept tiles, their C2T rows, h."""
-    row_of = {"f32": 4 * wl.d, "bf16": 2 * wl.d, "int4": wl.d // 2 + 2 * (wl.d // 128)}
-    row = row_of[wl.e_pack]
-    csz = 4 if wl.dtype == "f32" else 2
-    c_bytes = wl.c * row_of[wl.c_dtype]
-    tile_bytes = B * wl.p * wl.b * (row + 4)
-    return c_bytes, tile_bytes, c_bytes + tile_bytes + B * wl.d * csz
+def row_bytes(fmt: str, d: int) -> int:
+    return {"f32": 4 * d, "bf16": 2 * d, "int4": d // 2 + 2 * (d // 128)}[fmt]
+
+
+def algorithmic_bytes(wl, B, union=None):
+    """Bytes a call must read at least: the centroids, the kept tiles with their C2T rows, h.
+    B > 1 reads each kept tile once for all rows that kept it: `union` distinct clusters."""
+    c_bytes = wl.c * row_bytes(wl.c_dtype, wl.d)
+    kept = B * wl.p if union is None else union
+    tile_bytes = int(round(kept * wl.b * (row_bytes(wl.e_pack, wl.d) + 4)))
+    h_bytes = B * wl.d * (4 if wl.dtype == "f32" else 2)
+    return c_bytes, tile_bytes, c_bytes + tile_bytes + h_bytes
 
 
 def source_sha256() -> str:
@@ -58,13 +71,13 @@ def source_sha256() -> str:
 
 
 def measured_traffic(workload: str, kernels) -> "int | None":
-    """HBM bytes per launch of `kernels` (name prefixes) from profiles/hbm_traffic_<workload>_b1.txt.
+    """HBM bytes per launch of `kernels` (name prefixes) from profiles/hbm_traffic_<workload>.txt.
 
     That file holds FETCH_SIZE / WRITE_SIZE per dispatch from two rocprofv3 --pmc runs of
     this script, scaled by the factors a plain 1 GiB copy gave.  None when it is missing or
     was taken on other library sources than the ones built now.
     """
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_b1.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     sha, found = None, {}
@@ -85,35 +98,60 @@ def measured_traffic(workload: str, kernels) -> "int | None":
     return total
 
 
-def time_graph(torch, launch, n_calls, reps, warm_reps=2):
-    """Capture n_calls launches in one graph; return seconds per call over `reps` replays."""
+def capture(torch, launch, n_calls, first=0):
+    """A graph of launch(first) .. launch(first + n_calls - 1) (captured, not executed)."""
+    g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for i in range(n_calls):          # eager warm-up on the capture stream
-            launch(i)
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + n_calls):
+                launch(i)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(n_calls):
-            launch(i)
-    for _ in range(warm_reps):
-        g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    return g
+
+
+def replay_times(torch, g, n_calls, reps):
+    """Seconds per call of each of `reps` replays of g, each timed alone with HIP events."""
+    out = []
     for _ in range(reps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
         g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / (reps * n_calls), g
+        a1.record()
+        torch.cuda.synchronize()
+        out.append(a0.elapsed_time(a1) * 1e-3 / n_calls)
+    return out
 
 
-def cpu_baseline(wl, hd, C2T, budget_s=15.0):
-    """The oracle forward (fp64 NumPy) on the host cores: a bounded sample of calls."""
+def graph_seconds_per_call(torch, launch, n_calls, reps):
+    """Eager warm-up of every call, then the median over `reps` replays of an n_calls graph."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    for i in range(n_calls):
+        launch(i)
+    torch.cuda.synchronize()
+    g = capture(torch, launch, n_calls)
+    g.replay()
+    torch.cuda.synchronize()
+    t = float(np.median(replay_times(torch, g, n_calls, reps)))
+    del g
+    return t
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
+def cpu_baseline(wl, hd, C2T, threads: int, budget_s: float):
+    """The oracle forward (fp64 NumPy) on `threads` host threads: a bounded sample of calls."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import head as ohead
     from oracle import kmeans
@@ -121,34 +159,227 @@ def cpu_baseline(wl, hd, C2T, budget_s=15.0):
     C = kmeans.centroids_from_c2t(Ev, C2T, wl.c_dtype)
     del Ev
     tiles = ohead.pack_tiles(hd.E, wl.dtype, C2T, wl.e_pack)
-    ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)        # warm-up
-    n, t0 = 0, time.perf_counter()
-    while True:
-        ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or n >= 200:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    model = "unknown CPU"
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)        # warm-up
+        n, t0 = 0, time.perf_counter()
+        while True:
+            ohead.forward(hd.h, wl.dtype, C, wl.c_dtype, C2T, tiles, wl.p)
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or n >= 200:
                 break
-    except OSError:
-        pass
-    return {"value": n / dt, "unit": "calls/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} greedy oracle.head.forward calls (B=1, full workload shape) in {dt:.1f} s "
-                      f"on {model}"}
+    return {"value": round(n / dt, 3), "unit": "calls/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n} greedy oracle.head.forward calls (B=1, full {wl.name} head shape) in {dt:.1f} s "
+                      f"on {used} thread(s) of a {cpu_model()}, {os.cpu_count()} logical CPUs"}
+
+
+class Head:
+    """One workload's head on the GPU with R rotated copies of its centroids and tiles."""
+
+    def __init__(self, name: str, R: int = 0, dense=True):
+        import numpy as np
+        import torch
+
+        import workloads
+        from clustered_retrieval_lm_amd import flashhead as fh
+        from clustered_retrieval_lm_amd.head import DeviceHead, to_device
+        self.torch, self.fh = torch, fh
+        self.lib = fh.load_library()
+        wl = workloads.WORKLOADS[name]
+        self.wl = wl
+        cfile = {"int4_b16": "int4", "gemma_c4": "gemma"}.get(name, name)
+        self.C2T = np.load(os.path.join(ROOT, "tests", "golden", f"clusters_{cfile}.npz"))["C2T"]
+        t0 = time.perf_counter()
+        self.hd = workloads.make_head(wl)
+        self.dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, self.C2T, self.hd.E, wl.dtype, wl.c_dtype, wl.e_pack,
+                                            wl.dtype, device="cuda", keep_dense=dense)
+        _, _, per_call = algorithmic_bytes(wl, wl.B)
+        self.R = R or max(2, int(np.ceil(4 * MALL_BYTES / max(per_call, 1))))
+        dv = self.dev
+        self.Cs_by = {wl.c_dtype: [dv.C] + [dv.C.clone() for _ in range(self.R - 1)]}
+        self.Ts = [dv.tiles] + [dv.tiles.clone() for _ in range(self.R - 1)]
+        self.Ss = [dv.scales] + [dv.scales.clone() if dv.scales is not None else None for _ in range(self.R - 1)]
+        self.Hs = {}
+        self.to_device = to_device
+        log(f"{name}: B={wl.B} d={wl.d} V={wl.V} c={wl.c} p={wl.p} {wl.dtype}/{wl.c_dtype}/{wl.e_pack}, "
+            f"{self.R} rotated copies ({self.R * (dv.C.numel() + dv.tiles.numel()) / 2**30:.2f} GiB), "
+            f"built in {time.perf_counter() - t0:.1f} s")
+
+    def centroids(self, c_dtype: str):
+        """R copies of the centroids stored as c_dtype (computed on the GPU from E and C2T)."""
+        if c_dtype not in self.Cs_by:
+            torch, fh, dv, wl = self.torch, self.fh, self.dev, self.wl
+            desc = fh.make_desc(1, wl.d, wl.V, wl.c, wl.dtype, c_dtype, wl.e_pack)
+            C = torch.empty(fh.flashhead_centroids_bytes(desc), dtype=torch.uint8, device="cuda")
+            fh.flashhead_centroids(desc, wl.dtype, dv.E if dv.E is not None else self.to_device(self.hd.E, "cuda"),
+                                   dv.c2t, C)
+            self.Cs_by[c_dtype] = [C] + [C.clone() for _ in range(self.R - 1)]
+        return self.Cs_by[c_dtype]
+
+    @property
+    def Cs(self):
+        return self.Cs_by[self.wl.c_dtype]
+
+    def desc(self, B: int, c_dtype=None, e_dtype=None):
+        wl = self.wl
+        return self.fh.make_desc(B, wl.d, wl.V, wl.c, wl.dtype, c_dtype or wl.c_dtype, e_dtype or wl.e_pack)
+
+    def hidden(self, B: int):
+        """R distinct hidden-state batches [B][d] (the workload's own h first)."""
+        import workloads
+        if B not in self.Hs:
+            wl = self.wl
+            first = self.hd.h if B == wl.B else workloads.make_hidden(wl, B, seed=900 + B)
+            self.Hs[B] = [self.to_device(first, "cuda")] + [
+                self.to_device(workloads.make_hidden(wl, B, seed=1000 + 37 * B + r), "cuda") for r in range(1, self.R)]
+        return self.Hs[B]
+
+    def launcher(self, B, p, mode, tau, ws, fo, rotate=True, entry="forward", wss=None, c_dtype=None):
+        torch, fh, lib, dv, wl = self.torch, self.fh, self.lib, self.dev, self.wl
+        c_dtype = c_dtype or wl.c_dtype
+        desc = self.desc(B, c_dtype)
+        Cs = self.centroids(c_dtype)
+        Hs = self.hidden(B)
+        m = fh.MODES[mode]
+        R = self.R if rotate else 1
+
+        def fwd(i):
+            r = i % R
+            st = lib.flashhead_forward(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(), dv.c2t.data_ptr(),
+                                       self.Ts[r].data_ptr(), self.Ss[r].data_ptr() if self.Ss[r] is not None else None,
+                                       p, m, tau, wl.sample_seed, i, ws.data_ptr(), ws.numel(), ctypes.byref(fo),
+                                       torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        def scores(i):
+            r = i % R
+            st = lib.flashhead_centroid_scores(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(), m, tau,
+                                               wl.sample_seed, i, ws.data_ptr(), ws.numel(), None,
+                                               torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        def stage2(i):                       # over R workspaces that hold the R batches' keys
+            r = i % R
+            st = lib.flashhead_select_and_probe(ctypes.byref(desc), p, Hs[r].data_ptr(), dv.c2t.data_ptr(),
+                                                self.Ts[r].data_ptr(),
+                                                self.Ss[r].data_ptr() if self.Ss[r] is not None else None, m, tau,
+                                                wl.sample_seed, r, wss[r].data_ptr(), wss[r].numel(), ctypes.byref(fo),
+                                                torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        return {"forward": fwd, "scores": scores, "stage2": stage2}[entry]
+
+    def kept_union(self, B, p, mode, tau):
+        """Mean number of distinct clusters the B rows keep per call (over the R batches)."""
+        import numpy as np
+        torch, fh, dv, wl = self.torch, self.fh, self.dev, self.wl
+        if B == 1:
+            return None
+        desc = self.desc(B)
+        ws = dv.workspace(B, p)
+        ids = torch.empty(B, p, dtype=torch.int32, device="cuda")
+        sizes = []
+        for r, h in enumerate(self.hidden(B)):
+            fh.flashhead_centroid_scores(desc, h, self.Cs[r], mode, tau, wl.sample_seed, r, ws)
+            fh.flashhead_select_probes(desc, p, ws, ids)
+            sizes.append(int(torch.unique(ids).numel()))
+        return float(np.mean(sizes))
+
+    def dense_seconds(self, B, mode, tau, int4=False):
+        """Seconds per call of flashhead_dense_forward over the full E (bf16, or int4-g128 rows)."""
+        torch, fh, lib, dv, wl = self.torch, self.fh, self.lib, self.dev, self.wl
+        if int4:
+            E = self.int4_dense()
+            if E is None:
+                return None, None
+            ddesc = self.desc(B, e_dtype="int4")
+            nbytes = wl.V * row_bytes("int4", wl.d)
+        else:
+            E = dv.E
+            ddesc = self.desc(B, e_dtype=wl.dtype)
+            nbytes = wl.V * row_bytes(wl.dtype, wl.d)
+        dws = torch.empty(fh.flashhead_dense_workspace_bytes(ddesc), dtype=torch.uint8, device="cuda")
+        dtok = torch.empty(B, dtype=torch.int32, device="cuda")
+        E2 = [E, E.clone()]
+        Hs = self.hidden(B)
+
+        def dense_call(i):
+            st = lib.flashhead_dense_forward(ctypes.byref(ddesc), Hs[i % len(Hs)].data_ptr(), E2[i % 2].data_ptr(),
+                                             fh.MODES[mode], tau, wl.sample_seed, i, dws.data_ptr(), dws.numel(),
+                                             dtok.data_ptr(), None, torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        t = graph_seconds_per_call(torch, dense_call, 20, 5)
+        del E2
+        return t, nbytes
+
+    def int4_dense(self):
+        """The token-major int4-g128 E (nibbles [V][d/2], then the bf16 scales), quantised on the GPU
+        from the bf16 E by flashhead_centroids over one-token clusters -- the rule that packed the
+        int4 tiles."""
+        if getattr(self, "_e4", None) is not None:
+            return self._e4
+        import numpy as np
+        torch, fh, dv, wl = self.torch, self.fh, self.dev, self.wl
+        if dv.E is None or wl.dtype != "bf16":
+            return None
+        d1 = fh.make_desc(1, wl.d, wl.V, wl.V, wl.dtype, "int4", "int4")
+        ident = self.to_device(np.arange(wl.V, dtype=np.int32).reshape(wl.V, 1), "cuda")
+        e4 = torch.empty(fh.flashhead_centroids_bytes(d1), dtype=torch.uint8, device="cuda")
+        fh.flashhead_centroids(d1, wl.dtype, dv.E, ident, e4)
+        torch.cuda.synchronize()
+        self._e4 = e4
+        return e4
+
+
+def measure_config(hd: Head, cfg, mode: str):
+    """calls/s, achieved GB/s for one configuration (median of graph replays); `cfg` is the
+    configuration's workload (its B, p, temperature and centroid dtype) on the head `hd`."""
+    torch, fh, dv = hd.torch, hd.fh, hd.dev
+    B, p = cfg.B, cfg.p
+    tau = (cfg.temperatures[0] if cfg.temperatures else 1.0) if mode == "sample" else 1.0
+    ws = torch.empty(fh.flashhead_workspace_bytes(hd.desc(B, cfg.c_dtype), p), dtype=torch.uint8, device="cuda")
+    out = dv.outputs(B, p, probes=False)
+    fo = fh.make_outputs(out["token"])
+    union = hd.kept_union(B, p, mode, tau)
+    c_bytes, tile_bytes, alg = algorithmic_bytes(cfg, B, union)
+    n = max(CONFIG_CALLS // hd.R, 1) * hd.R
+    t = graph_seconds_per_call(torch, hd.launcher(B, p, mode, tau, ws, fo, c_dtype=cfg.c_dtype), n, CONFIG_REPLAYS)
+    res = {"workload": f"{cfg.name} B={B} d={cfg.d} V={cfg.V} c={cfg.c} p={p} {cfg.c_dtype} C, {cfg.e_pack} tiles, "
+                       f"{mode}" + (f" tau={tau}" if mode == "sample" else ""),
+           "calls_per_s": round(1.0 / t, 1), "us_per_call": round(t * 1e6, 3), "algorithmic_bytes": alg,
+           "achieved_GBps": round(alg / t / 1e9, 1), "frac_of_peak": round(alg / t / 1e9 / PEAK_HBM_GBS, 4)}
+    if union is not None:
+        res["kept_union_clusters"] = round(union, 1)
+    return res, t, alg
+
+
+def dense_block(hd: Head, mode: str, t_call: float, alg: int, B: int, tau: float):
+    """The dense head over the same E (bf16, and int4-g128 rows for the int4 heads) against a
+    FlashHead call of t_call seconds that reads `alg` bytes."""
+    wl = hd.wl
+    out = {}
+    for kind in (["bf16", "int4"] if wl.e_pack == "int4" else [wl.dtype]):
+        t_d, nbytes = hd.dense_seconds(B, mode, tau, int4=(kind == "int4"))
+        if t_d is None:
+            out[kind] = None
+            continue
+        out[kind] = {"us_per_call": round(t_d * 1e6, 2), "bytes": nbytes, "achieved_GBps": round(nbytes / t_d / 1e9, 1),
+                     "speedup": round(t_d / t_call, 2), "byte_ratio": round(nbytes / alg, 2)}
+    return out
 
 
 def run_sweep(args) -> int:
     """The clusters / probes grid of the paper's Table 7 at the Llama-3.2-1B head shape
     (d = 2048, V = 128256, bf16): c in {4008, 8016, 16032} (b = 32, 16, 8), p in {128, 256, 512},
-    greedy, B = 1, timed like the main bench (graph replay over R centroid copies and R hidden
-    states), with the dense head as the comparator.  Synthetic heads of the workloads recipe
-    whose latent partition serves as the balanced clustering (latency does not depend on
+    greedy, B = 1, timed like the configurations (graph replay over R centroid / tile copies and
+    R hidden states), with the dense head as the comparator.  Synthetic heads of the workloads
+    recipe whose latent partition serves as the balanced clustering (latency does not depend on
     which balanced clustering is used).  Prints one JSON line."""
     import numpy as np
     import torch
@@ -159,7 +390,6 @@ def run_sweep(args) -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     lib = fh.load_library()
-    import ctypes
     d, V = 2048, 128256
     rows, dense = [], None
     for ci, c in enumerate((4008, 8016, 16032)):
@@ -170,6 +400,7 @@ def run_sweep(args) -> int:
         dev = DeviceHead.from_clusters(d, V, c, C2T, hd.E, "bf16", "bf16", "bf16", "bf16", device="cuda",
                                        keep_dense=dense is None)
         Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
+        Ts = [dev.tiles] + [dev.tiles.clone() for _ in range(R - 1)]
         Hs = [to_device(hd.h[r:r + 1], "cuda") for r in range(R)]
         desc = dev.desc(1)
         for p in (128, 256, 512):
@@ -179,14 +410,13 @@ def run_sweep(args) -> int:
 
             def fwd(i):
                 st = lib.flashhead_forward(ctypes.byref(desc), Hs[i % R].data_ptr(), Cs[i % R].data_ptr(),
-                                           dev.c2t.data_ptr(), dev.tiles.data_ptr(), None, p, 0, 1.0, 0, i,
+                                           dev.c2t.data_ptr(), Ts[i % R].data_ptr(), None, p, 0, 1.0, 0, i,
                                            ws.data_ptr(), ws.numel(), ctypes.byref(fo),
                                            torch.cuda.current_stream().cuda_stream)
                 if st != 0:
                     raise fh.FlashHeadError(st, fh.flashhead_last_error())
 
-            t, g = time_graph(torch, fwd, 8 * R, 20, warm_reps=2)
-            del g
+            t = graph_seconds_per_call(torch, fwd, 8 * R, 10)
             alg = c * d * 2 + p * b * (2 * d + 4) + 2 * d
             rows.append({"c": c, "b": b, "p": p, "us_per_call": round(t * 1e6, 2),
                          "calls_per_s": round(1.0 / t, 1), "algorithmic_bytes": alg,
@@ -204,12 +434,12 @@ def run_sweep(args) -> int:
                 if st != 0:
                     raise fh.FlashHeadError(st, fh.flashhead_last_error())
 
-            t_d, g = time_graph(torch, dense_call, 20, 10, warm_reps=1)
-            del g, E2
+            t_d = graph_seconds_per_call(torch, dense_call, 20, 5)
+            del E2
             dense = {"us_per_call": round(t_d * 1e6, 2), "bytes": V * d * 2,
                      "achieved_GBps": round(V * d * 2 / t_d / 1e9, 1)}
             log(f"dense head: {t_d * 1e6:.2f} us/call")
-        del dev, Cs, Hs, hd
+        del dev, Cs, Ts, Hs, hd
         torch.cuda.empty_cache()
     for r in rows:
         r["speedup_vs_dense"] = round(dense["us_per_call"] / r["us_per_call"], 2)
@@ -218,17 +448,24 @@ def run_sweep(args) -> int:
     return 0
 
 
+# configurations carried in the line besides the headline: (workload, mode)
+CONFIGS = [("gemma", "greedy"), ("gemma", "sample"), ("gemma_c4", "greedy"), ("gemma_c4", "sample"),
+           ("llama", "greedy"), ("qwen", "greedy"), ("qwen", "sample"), ("int4", "greedy"), ("int4", "sample"),
+           ("int4_b16", "greedy"), ("int4_b16", "sample")]
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2400)
-    ap.add_argument("--warmup", type=int, default=240)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gemma")
     ap.add_argument("--mode", default="greedy", choices=["greedy", "sample"])
     ap.add_argument("--rotate", type=int, default=0, help="copies of the head cycled through (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-head comparator")
     ap.add_argument("--no-mc", action="store_true", help="skip the Monte-Carlo marginal (N = 10^4 probe sets)")
+    ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
     ap.add_argument("--mc-sets", type=int, default=10000, help="probe sets of the Monte-Carlo marginal")
     ap.add_argument("--sweep", action="store_true",
                     help="only the clusters x probes grid (Table 7) at the Llama-3.2-1B head shape")
@@ -246,221 +483,124 @@ def main() -> int:
     import numpy as np
     import torch
 
-    import workloads
     from clustered_retrieval_lm_amd import flashhead as fh
-    from clustered_retrieval_lm_amd.head import DeviceHead, to_device
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     fh.load_library()
-    wl = workloads.WORKLOADS[args.workload]
-    cfile = {"int4_b16": "int4", "gemma_c4": "gemma"}.get(args.workload, args.workload)
-    C2T = np.load(os.path.join(ROOT, "tests", "golden", f"clusters_{cfile}.npz"))["C2T"]
-    log(f"workload {wl.name}: B={wl.B} d={wl.d} V={wl.V} c={wl.c} p={wl.p} {wl.dtype}/{wl.e_pack}")
-    hd = workloads.make_head(wl)
-    dev = DeviceHead.from_clusters(wl.d, wl.V, wl.c, C2T, hd.E, wl.dtype, wl.c_dtype, wl.e_pack, wl.dtype,
-                                   device="cuda", keep_dense=not args.no_dense)
-    c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, wl.B)
-    union_frac = None
-    R = args.rotate or max(2, int(np.ceil(4 * MALL_BYTES / max(alg_bytes, 1))))
-    log(f"rotating {R} copies of the centroids ({R * dev.C.numel() * dev.C.element_size() / 2**30:.2f} GiB) "
-        f"and {R} hidden states over one tile array ({dev.tiles.numel() / 2**30:.2f} GiB)")
-    Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
-    Ts = [dev.tiles] * R
-    Ss = [dev.scales] * R
-    Hs = [to_device(hd.h, "cuda")] + [to_device(workloads.make_hidden(wl, wl.B, seed=1000 + r), "cuda")
-                                      for r in range(1, R)]
+    K, W = max(1, args.steps), max(0, args.warmup)
+    hd = Head(args.workload, args.rotate, dense=not args.no_dense)
+    R_head = hd.R
+    wl, dv = hd.wl, hd.dev
     B, p = wl.B, wl.p
-    desc = dev.desc(B)
-    ws = dev.workspace(B, p)
-    out = dev.outputs(B, p, probes=False)
+    tau = (wl.temperatures[0] if wl.temperatures else 1.0) if args.mode == "sample" else 1.0
+    ws = dv.workspace(B, p)
+    out = dv.outputs(B, p, probes=False)
     fo = fh.make_outputs(out["token"])
-    tau = wl.temperatures[0] if (args.mode == "sample" and wl.temperatures) else 1.0
-    if B > 1:
-        # at B > 1 each kept tile is read once for all rows that kept it: the bytes a call must
-        # read are the union of the rows' probe sets (measured here on the R hidden states)
-        ids = torch.empty(B, p, dtype=torch.int32, device="cuda")
-        sizes = []
-        for r in range(R):
-            fh.flashhead_centroid_scores(desc, Hs[r], Cs[r], args.mode, tau, wl.sample_seed, r, ws)
-            fh.flashhead_select_probes(desc, p, ws, ids)
-            sizes.append(int(torch.unique(ids).numel()))
-        union = float(np.mean(sizes))
-        union_frac = union / (B * p)
-        row_b = tile_bytes // (B * p * wl.b)
-        tile_bytes = int(round(union * wl.b * row_b))
-        alg_bytes = c_bytes + tile_bytes + B * wl.d * (4 if wl.dtype == "f32" else 2)
-        log(f"B={B}: {union:.0f} distinct clusters kept per call on average ({B * p} probes)")
-    lib = fh.load_library()
-    wsb = ws.numel()
-    import ctypes
+    union = hd.kept_union(B, p, args.mode, tau)
+    c_bytes, tile_bytes, alg_bytes = algorithmic_bytes(wl, B, union)
+    fwd = hd.launcher(B, p, args.mode, tau, ws, fo)
 
-    def fwd(i):
-        r = i % R
-        st = lib.flashhead_forward(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(), dev.c2t.data_ptr(),
-                                   Ts[r].data_ptr(), Ss[r].data_ptr() if Ss[r] is not None else None, p,
-                                   fh.MODES[args.mode], tau, wl.sample_seed, i, ws.data_ptr(), wsb,
-                                   ctypes.byref(fo), torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise fh.FlashHeadError(st, fh.flashhead_last_error())
-
-    def scores(i):
-        r = i % R
-        st = lib.flashhead_centroid_scores(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(),
-                                           fh.MODES[args.mode], tau, wl.sample_seed, i, ws.data_ptr(), wsb, None,
-                                           torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise fh.FlashHeadError(st, fh.flashhead_last_error())
-
-    # ---- whole path: graph of G calls, replayed
-    G = R * max(1, 120 // R)
-    reps = max(1, -(-args.steps // G))
-    warm = max(1, -(-args.warmup // G))
-    steps = reps * G
-    log(f"timing {steps} steps ({reps} replays of a {G}-call graph) after {warm * G} warm-up steps")
+    # ---- the headline: W untimed calls, then exactly K timed calls (one graph replay)
+    g_warm = capture(torch, fwd, max(W, 1)) if W else None
+    g_timed = capture(torch, fwd, K, first=W)
+    if g_warm is not None:
+        g_warm.replay()
     torch.cuda.synchronize()
-    t_call, g_fwd = time_graph(torch, fwd, G, reps, warm_reps=warm)
-    calls_per_s = 1.0 / t_call
-    log(f"forward: {t_call * 1e6:.2f} us/call, {calls_per_s:.0f} calls/s, "
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g_timed.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_call = e0.elapsed_time(e1) * 1e-3 / K
+    log(f"headline: {K} timed calls after {W} warm-up calls: {t_call * 1e6:.2f} us/call, "
         f"{alg_bytes / t_call / 1e9:.0f} GB/s algorithmic")
-    # spread: each replay of the graph timed on its own (20 replays)
-    per = []
-    for _ in range(20):
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record()
-        g_fwd.replay()
-        a1.record()
-        torch.cuda.synchronize()
-        per.append(a0.elapsed_time(a1) * 1e3 / G)
-    spread = {"median": round(float(np.median(per)), 3), "p10": round(float(np.percentile(per, 10)), 3),
-              "p90": round(float(np.percentile(per, 90)), 3), "replays": len(per), "calls_per_replay": G}
-    log(f"forward per replay: median {spread['median']:.2f} us/call (p10 {spread['p10']:.2f}, p90 {spread['p90']:.2f})")
-    del g_fwd
+    per = replay_times(torch, g_timed, K, 20)
+    spread = {"median": round(float(np.median(per)) * 1e6, 3), "p10": round(float(np.percentile(per, 10)) * 1e6, 3),
+              "p90": round(float(np.percentile(per, 90)) * 1e6, 3), "replays": len(per), "calls_per_replay": K}
+    log(f"per replay of the {K}-call graph: median {spread['median']:.2f} us/call (p10 {spread['p10']:.2f}, "
+        f"p90 {spread['p90']:.2f})")
+    del g_warm, g_timed
 
-    # warm: the same centroids and hidden state every call (the centroids stay in the
-    # last-level cache) -- labelled, never the headline
-    def fwd_warm(i):
-        st = lib.flashhead_forward(ctypes.byref(desc), Hs[0].data_ptr(), Cs[0].data_ptr(), dev.c2t.data_ptr(),
-                                   Ts[0].data_ptr(), Ss[0].data_ptr() if Ss[0] is not None else None, p,
-                                   fh.MODES[args.mode], tau, wl.sample_seed, i, ws.data_ptr(), wsb,
-                                   ctypes.byref(fo), torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise fh.FlashHeadError(st, fh.flashhead_last_error())
-
-    t_warm, g_w = time_graph(torch, fwd_warm, G, max(1, reps // 2), warm_reps=1)
-    del g_w
-    log(f"forward, warm (no rotation): {t_warm * 1e6:.2f} us/call")
-
-    # pure-read ceiling of this GPU: a 2 GiB streaming reduction
-    big = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
-    for _ in range(2):
-        big.sum()
+    # ---- the two halves, each timed alone the same way; the warm (unrotated) call
+    n_unit = max(CONFIG_CALLS // hd.R, 1) * hd.R
+    t_sc = graph_seconds_per_call(torch, hd.launcher(B, p, args.mode, tau, ws, fo, entry="scores"), n_unit, 10)
+    sc_bytes = c_bytes + B * wl.d * (4 if wl.dtype == "f32" else 2) + B * wl.c * 4
+    wss = [torch.empty_like(ws) for _ in range(hd.R)]
+    for r in range(hd.R):
+        fh.flashhead_centroid_scores(hd.desc(B), hd.hidden(B)[r], hd.Cs[r], args.mode, tau, wl.sample_seed, r, wss[r])
     torch.cuda.synchronize()
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for _ in range(5):
-        big.sum()
-    r1.record()
-    torch.cuda.synchronize()
-    read_ceiling = big.numel() * 4 * 5 / (r0.elapsed_time(r1) * 1e-3) / 1e9
-    ceiling_src = "torch sum over 2 GiB"
-    del big
-    log(f"streaming read, torch sum over 2 GiB: {read_ceiling:.0f} GB/s")
+    t_s2 = graph_seconds_per_call(torch, hd.launcher(B, p, args.mode, tau, ws, fo, entry="stage2", wss=wss),
+                                  n_unit, 10)
+    s2_bytes = tile_bytes + B * wl.c * 4 + B * wl.d * (4 if wl.dtype == "f32" else 2)
+    del wss
+    t_warm = graph_seconds_per_call(torch, hd.launcher(B, p, args.mode, tau, ws, fo, rotate=False), n_unit, 10)
+    log(f"centroid scores {t_sc * 1e6:.2f} us, selection + stage 2 {t_s2 * 1e6:.2f} us, warm call {t_warm * 1e6:.2f} us")
 
-    # ---- the two halves of a call, each timed alone the same way: stage 1 (k_b1_scores) and
-    # selection + stage 2 (k_b1_stage2 + the one-block token decode), the latter over R
-    # workspaces that hold the stage-1 keys of the R hidden states
-    t_sc, g_sc = time_graph(torch, scores, G, reps, warm_reps=1)
-    sc_bytes = c_bytes + B * wl.d * 2 + B * wl.c * 4
-    log(f"centroid scores: {t_sc * 1e6:.2f} us/launch, {sc_bytes / t_sc / 1e9:.0f} GB/s")
-    del g_sc
-    wss = [torch.empty_like(ws) for _ in range(R)]
-    for r in range(R):
-        st = lib.flashhead_centroid_scores(ctypes.byref(desc), Hs[r].data_ptr(), Cs[r].data_ptr(),
-                                           fh.MODES[args.mode], tau, wl.sample_seed, r, wss[r].data_ptr(), wsb,
-                                           None, torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise fh.FlashHeadError(st, fh.flashhead_last_error())
-    torch.cuda.synchronize()
+    if B == 1:
+        units = {
+            "k_b1_scores (centroid scores, key histogram)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
+            "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
+                (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
+        }
+    else:
+        units = {
+            "k_mfma / k_scores_gemv (centroid scores)": (sc_bytes, t_sc, ["fh::k_mfma", "fh::k_scores_gemv"]),
+            "k_clear_select + k_select + k_tiles_mask + k_finalize (selection, probe logits, tokens)":
+                (s2_bytes, t_s2, ["fh::k_clear_select", "fh::k_select", "fh::k_tiles_mask", "fh::k_finalize"]),
+        }
+    dom = max(units, key=lambda k: units[k][1])
+    dom_bytes, dom_t, dom_kernels = units[dom]
+    dom_gbs = dom_bytes / dom_t / 1e9
+    tag = f"{args.workload}_b{B}" if args.mode == "greedy" else None
+    traffic = measured_traffic(tag, dom_kernels) if tag else None
 
-    def stage2(i):
-        r = i % R
-        st = lib.flashhead_select_and_probe(ctypes.byref(desc), p, Hs[r].data_ptr(), dev.c2t.data_ptr(),
-                                            Ts[r].data_ptr(), Ss[r].data_ptr() if Ss[r] is not None else None,
-                                            fh.MODES[args.mode], tau, wl.sample_seed, r, wss[r].data_ptr(), wsb,
-                                            ctypes.byref(fo), torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise fh.FlashHeadError(st, fh.flashhead_last_error())
-
-    t_s2, g_s2 = time_graph(torch, stage2, G, reps, warm_reps=1)
-    s2_bytes = tile_bytes + B * wl.c * 4 + B * wl.d * 2
-    log(f"selection + stage 2: {t_s2 * 1e6:.2f} us/call, {s2_bytes / t_s2 / 1e9:.0f} GB/s")
-    del g_s2, wss
-
+    # ---- comparators and the streaming-read ceiling
     dense = None
+    read_ceiling, ceiling_src = None, None
     if not args.no_dense:
-        dws = torch.empty(fh.flashhead_dense_workspace_bytes(dev.desc(B, e_dtype=wl.dtype)), dtype=torch.uint8,
-                          device="cuda")
-        dtok = torch.empty(B, dtype=torch.int32, device="cuda")
-        ddesc = dev.desc(B, e_dtype=wl.dtype)
-        E2 = [dev.E, dev.E.clone()]
-
-        def dense_call(i):
-            st = lib.flashhead_dense_forward(ctypes.byref(ddesc), Hs[i % R].data_ptr(), E2[i % 2].data_ptr(),
-                                             fh.MODES[args.mode], tau, wl.sample_seed, i, dws.data_ptr(),
-                                             dws.numel(), dtok.data_ptr(), None,
-                                             torch.cuda.current_stream().cuda_stream)
-            if st != 0:
-                raise fh.FlashHeadError(st, fh.flashhead_last_error())
-
-        t_d, g_d = time_graph(torch, dense_call, 20, 10, warm_reps=1)
-        dense_bytes = wl.V * wl.d * (2 if wl.dtype == "bf16" else 4)
-        # secondary comparator: torch's linear + argmax on the same E (its library GEMV/GEMM)
+        dense = dense_block(hd, args.mode, t_call, alg_bytes, B, tau)
+        dd = dense.get(wl.dtype)
+        if dd:
+            read_ceiling, ceiling_src = dd["achieved_GBps"], f"flashhead_dense_forward streaming {dd['bytes'] / 1e6:.0f} MB"
         tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        Et = [x.view(tdt).view(wl.V, wl.d) for x in E2]
-        Ht = [x.view(tdt).view(B, wl.d) for x in Hs]
-
-        def torch_call(i):
-            torch.argmax(torch.nn.functional.linear(Ht[i % R], Et[i % 2]), dim=-1)
-
-        t_t, g_t = time_graph(torch, torch_call, 20, 10, warm_reps=1)
-        del g_t, Et, Ht
-        dense = {"calls_per_s": round(1.0 / t_d, 1), "us_per_call": round(t_d * 1e6, 2),
-                 "achieved_GBps": round(dense_bytes / t_d / 1e9, 1), "bytes": dense_bytes,
-                 "speedup": round(t_d / t_call, 2), "byte_ratio": round(dense_bytes / alg_bytes, 2),
-                 "torch_linear_argmax_us": round(t_t * 1e6, 2)}
-        log(f"torch linear + argmax on the same E: {t_t * 1e6:.1f} us/call")
-        if dense_bytes / t_d / 1e9 > read_ceiling:         # the dense GEMV streams E at a higher rate
-            read_ceiling = dense_bytes / t_d / 1e9
-            ceiling_src = f"flashhead_dense_forward streaming {dense_bytes / 1e6:.0f} MB"
-        log(f"dense head: {t_d * 1e6:.1f} us/call, {dense_bytes / t_d / 1e9:.0f} GB/s; "
-            f"FlashHead speedup {t_d / t_call:.2f}x (byte ratio {dense_bytes / alg_bytes:.2f}x)")
-        del g_d, E2
+        Et = dv.E.view(tdt).view(wl.V, wl.d)
+        Ht = [x.view(tdt).view(B, wl.d) for x in hd.hidden(B)]
+        t_t = graph_seconds_per_call(torch, lambda i: torch.argmax(torch.nn.functional.linear(Ht[i % len(Ht)], Et),
+                                                                   dim=-1), 20, 5)
+        dense["torch_linear_argmax_us"] = round(t_t * 1e6, 2)
+        log(f"dense head {dense}")
+    big = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
+    t_big = graph_seconds_per_call(torch, lambda i: big.sum(), 5, 3)
+    sum_gbs = big.numel() * 4 / t_big / 1e9
+    del big
+    if read_ceiling is None or sum_gbs > read_ceiling:
+        read_ceiling, ceiling_src = sum_gbs, "torch sum over 2 GiB"
 
     mc = None
     if not args.no_mc:
         # Appendix D.1's estimator: N probe sets per hidden state, the whole-vocabulary estimate
+        desc = hd.desc(B)
         mws = torch.empty(fh.flashhead_mc_marginal_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
         mout = torch.empty(B, wl.V, dtype=torch.float64, device="cuda")
         n_mc = args.mc_sets
+        Hs = hd.hidden(B)
 
         def mc_call(i):
-            fh.flashhead_mc_marginal(desc, Hs[i % R], Cs[i % R], dev.c2t, Ts[i % R], Ss[i % R], p, 1.0,
-                                     wl.sample_seed, n_mc, True, mws, mout)
+            fh.flashhead_mc_marginal(desc, Hs[i % hd.R], hd.Cs[i % hd.R], dv.c2t, hd.Ts[i % hd.R], hd.Ss[i % hd.R], p,
+                                     1.0, wl.sample_seed, n_mc, True, mws, mout)
 
         mc_call(0)
         torch.cuda.synchronize()
-        reps_mc = 5
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(reps_mc):
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record()
+        for i in range(5):
             mc_call(i)
-        e1.record()
+        m1.record()
         torch.cuda.synchronize()
-        t_mc = e0.elapsed_time(e1) / 1e3 / reps_mc
+        t_mc = m0.elapsed_time(m1) / 1e3 / 5
         mc = {"n_sets": n_mc, "p": p, "tau": 1.0, "ms_per_call": round(t_mc * 1e3, 3),
               "sets_per_s": round(B * n_mc / t_mc, 0), "us_per_set": round(t_mc * 1e6 / (B * n_mc), 4)}
-        log(f"Monte-Carlo marginal: {n_mc} probe sets in {t_mc * 1e3:.2f} ms "
-            f"({B * n_mc / t_mc:.3g} sets/s)")
+        log(f"Monte-Carlo marginal: {n_mc} probe sets in {t_mc * 1e3:.2f} ms")
         del mws, mout
 
     if args.copy_calib:
@@ -474,32 +614,50 @@ def main() -> int:
     cpu = None
     if not args.no_cpu:
         log("oracle baseline on the host cores ...")
-        cpu = cpu_baseline(wl, hd, C2T)
-        log(f"oracle: {cpu['value']:.2f} calls/s on {cpu['cores']} threads")
+        nthreads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        cpu = cpu_baseline(wl, hd.hd, hd.C2T, nthreads, 12.0)
+        cpu["single_thread"] = cpu_baseline(wl, hd.hd, hd.C2T, 1, 12.0)
+        log(f"oracle: {cpu['value']} calls/s on {cpu['cores']} threads, "
+            f"{cpu['single_thread']['value']} calls/s on 1 thread")
 
-    if B == 1:
-        units = {
-            "k_b1_scores (centroid scores)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
-            "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
-                (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
-        }
-    else:
-        units = {
-            "k_mfma / k_scores_gemv (centroid scores)": (sc_bytes, t_sc, ["fh::k_mfma", "fh::k_scores_gemv"]),
-            "k_select + k_tiles_mask + k_finalize (selection, probe logits, tokens)":
-                (s2_bytes, t_s2, ["fh::k_select", "fh::k_tiles_mask", "fh::k_finalize"]),
-        }
-    dom = max(units, key=lambda k: units[k][1])
-    dom_bytes, dom_t, dom_kernels = units[dom]
-    dom_gbs = dom_bytes / dom_t / 1e9
-    traffic = measured_traffic(args.workload, dom_kernels) if args.mode == "greedy" else None
+    # ---- the other configurations, each head built once
+    configs = None
+    if not args.no_configs:
+        import workloads
+        configs = []
+        bases = {}
+        for name, mode in CONFIGS:
+            if name == args.workload and mode == args.mode:
+                continue
+            base = {"int4_b16": "int4", "gemma_c4": "gemma"}.get(name, name)
+            bases.setdefault(base, []).append((name, mode))
+        for base, items in bases.items():
+            if base == wl.name:
+                h2 = hd
+            else:
+                if hd is not None:
+                    del hd
+                    hd = None
+                torch.cuda.empty_cache()
+                h2 = Head(base, dense=not args.no_dense)
+            for name, mode in items:
+                cfg = workloads.WORKLOADS[name]
+                r, t2, alg2 = measure_config(h2, cfg, mode)
+                if not args.no_dense:
+                    tau2 = (cfg.temperatures[0] if cfg.temperatures else 1.0) if mode == "sample" else 1.0
+                    r["dense"] = dense_block(h2, mode, t2, alg2, cfg.B, tau2)
+                log(f"config {r['workload']}: {r['us_per_call']} us/call, {r['achieved_GBps']} GB/s, "
+                    f"dense {r.get('dense')}")
+                configs.append(r)
+            if h2 is not hd:
+                del h2
     res = {
         "metric": "head calls/s + achieved HBM GB/s vs dense LM head, B=1 Gemma-3-1B shape",
-        "value": round(calls_per_s, 1),
+        "value": round(1.0 / t_call, 1),
         "unit": "calls/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warm * G,
+        "steps": K,
+        "warmup": W,
         "ms_per_step": round(t_call * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -508,26 +666,26 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"{wl.name} head (B={B}, d={wl.d}, V={wl.V}, c={wl.c}, b={wl.b}, p={p}, "
                                f"{wl.c_dtype} C, {wl.dtype} h, {wl.e_pack} tiles, {args.mode})",
-                   "mode": args.mode, "rotated_copies": R},
+                   "mode": args.mode, "rotated_copies": R_head},
         "achieved_GBps": round(alg_bytes / t_call / 1e9, 1),
         "algorithmic_bytes": alg_bytes,
         "us_per_call_spread": spread,
         "warm_us_per_call": round(t_warm * 1e6, 3),
         "read_ceiling": {"GBps": round(read_ceiling, 1), "source": ceiling_src,
                          "frac": round(alg_bytes / t_call / 1e9 / read_ceiling, 4)},
-        "kept_union_fraction": None if union_frac is None else round(union_frac, 4),
-        # the batched centroid GEMM on MFMA (B > 1, bf16): its arithmetic rate against the dense
-        # bf16 MFMA peak (it is bound by the centroid bytes: B flop per byte read)
+        "kept_union_clusters": None if union is None else round(union, 1),
         "stage1_mfma": None if B == 1 else {
-            "tflops": round(2.0 * B * wl.c * wl.d / t_sc / 1e12, 2), "peak_tflops": 2500.0,
-            "frac": round(2.0 * B * wl.c * wl.d / t_sc / 1e12 / 2500.0, 5)},
+            "tflops": round(2.0 * B * wl.c * wl.d / t_sc / 1e12, 2), "peak_tflops": PEAK_BF16_TFLOPS,
+            "frac": round(2.0 * B * wl.c * wl.d / t_sc / 1e12 / PEAK_BF16_TFLOPS, 5)},
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_t * 1e6, 3)},
+                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_t * 1e6, 3),
+                     "whole_call_frac": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels": {k: {"bytes_per_launch": b_, "us_per_launch": round(t_ * 1e6, 3),
                         "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_, _) in units.items()},
         "dense": dense,
+        "configs": configs,
         "mc_marginal": mc,
         "cpu_baseline": cpu,
     }
