@@ -443,8 +443,49 @@ def run_sweep(args) -> int:
         torch.cuda.empty_cache()
     for r in rows:
         r["speedup_vs_dense"] = round(dense["us_per_call"] / r["us_per_call"], 2)
+
+    # equal against unequal clusters (Table 6's latency column): the c = 8016 head above, and the
+    # same head's tokens cut into 8016 clusters of lognormal sizes (workloads.make_unequal_clusters)
+    # given to the library as the padded dense C2T of Section 3.1 (b = the largest cluster)
+    c = 8016
+    hd = workloads.make_small(d, V, c, 16, seed=501, sigma_c=0.02, sigma_n=0.01, dtype="bf16")
+    C2T, sizes = workloads.make_unequal_clusters(hd.latent, c, seed=77)
+    bmax = C2T.shape[1]
+    R = max(4, int(np.ceil(2 * MALL_BYTES / (256 * bmax * (2 * d + 4)))))
+    dev = DeviceHead.from_clusters(d, c * bmax, c, C2T, hd.E, "bf16", "bf16", "bf16", "bf16", device="cuda")
+    Cs = [dev.C] + [dev.C.clone() for _ in range(R - 1)]
+    Ts = [dev.tiles] + [dev.tiles.clone() for _ in range(R - 1)]
+    Hs = [to_device(hd.h[r % 16:r % 16 + 1], "cuda") for r in range(R)]
+    desc = dev.desc(1)
+    unequal = []
+    for p in (128, 256, 512):
+        ws = dev.workspace(1, p)
+        out = dev.outputs(1, p, probes=False)
+        fo = fh.make_outputs(out["token"])
+
+        def fwd_u(i):
+            st = lib.flashhead_forward(ctypes.byref(desc), Hs[i % R].data_ptr(), Cs[i % R].data_ptr(),
+                                       dev.c2t.data_ptr(), Ts[i % R].data_ptr(), None, p, 0, 1.0, 0, i,
+                                       ws.data_ptr(), ws.numel(), ctypes.byref(fo),
+                                       torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise fh.FlashHeadError(st, fh.flashhead_last_error())
+
+        t = graph_seconds_per_call(torch, fwd_u, 8 * R, 10)
+        eq = [r for r in rows if r["c"] == c and r["p"] == p][0]
+        unequal.append({"p": p, "unequal_us_per_call": round(t * 1e6, 2), "equal_us_per_call": eq["us_per_call"],
+                        "unequal_over_equal": round(t * 1e6 / eq["us_per_call"], 2),
+                        "rows_read_per_call": p * bmax, "equal_rows_read_per_call": p * (V // c)})
+        log(f"unequal clusters (b_max={bmax}) p={p}: {t * 1e6:.2f} us/call vs equal {eq['us_per_call']} us")
+    del dev, Cs, Ts, Hs, hd
+    torch.cuda.empty_cache()
     print(json.dumps({"sweep": "clusters x probes (FlashHead Table 7 grid), Llama-3.2-1B head shape, bf16, "
-                               "B=1, greedy, synthetic", "dense": dense, "rows": rows}), flush=True)
+                               "B=1, greedy, synthetic", "dense": dense, "rows": rows,
+                      "unequal_clusters": {"what": "Table 6 ablation: 8016 clusters of lognormal sizes (sigma 0.5, "
+                                                   "mean 16) as a C2T padded to the largest cluster",
+                                           "b_max": int(bmax), "size_min": int(sizes.min()),
+                                           "size_mean": round(float(sizes.mean()), 2), "rows": unequal}}),
+          flush=True)
     return 0
 
 

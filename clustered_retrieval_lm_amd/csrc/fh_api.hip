@@ -139,21 +139,22 @@ fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E, 
   if (!int4 && E_scales) return fail(FH_ERR_ARG, "E_scales must be NULL unless e_dtype is INT4_G128");
   hipStream_t s = (hipStream_t)stream;
   const int V = (int)desc->V;
-  uint32_t* scratch = nullptr;   // counts[V], bad
-  hipError_t e = hipMalloc(&scratch, (size_t)(V + 1) * sizeof(uint32_t));
+  uint32_t* tmp = nullptr;   // counts[V], the empty-slot count, the error flags
+  hipError_t e = hipMalloc(&tmp, (size_t)(V + 2) * sizeof(uint32_t));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc");
-  e = hipMemsetAsync(scratch, 0, (size_t)(V + 1) * sizeof(uint32_t), s);
+  e = hipMemsetAsync(tmp, 0, (size_t)(V + 2) * sizeof(uint32_t), s);
   if (e == hipSuccess)
     e = fh::launch_pack(V, (int)desc->d, (int)desc->c, (int)(desc->V / desc->c), src_dtype == FH_BF16,
-                        fmt_of(desc->e_dtype), E, cluster_tokens, E_tiles, (uint16_t*)E_scales, scratch,
-                        scratch + V, s);
+                        fmt_of(desc->e_dtype), E, cluster_tokens, E_tiles, (uint16_t*)E_scales, tmp,
+                        tmp + V + 1, s);
   uint32_t bad = 0;
-  if (e == hipSuccess) e = hipMemcpyAsync(&bad, scratch + V, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(&bad, tmp + V + 1, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
-  hipError_t e2 = hipFree(scratch);
+  hipError_t e2 = hipFree(tmp);
   if (e != hipSuccess) return hip_fail(e, "flashhead_pack");
   if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
-  if (bad) return fail(FH_ERR_ARG, "cluster_tokens is not a permutation of [0, V)");
+  if (bad)
+    return fail(FH_ERR_ARG, "cluster_tokens must hold the tokens 0 .. n-1 once each and -1 in its other slots");
   return FH_OK;
 }
 
@@ -333,24 +334,40 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
                           sampling_of(mode, temperature, seed, step), ws, out, false, (hipStream_t)stream);
 }
 
-fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
+// The forward path of flashhead_forward on a carved workspace.
+static fh_status forward_on(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
                             const void* E_tiles, const void* E_scales, int64_t p, int32_t mode, float temperature,
-                            uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
-                            const fh_outputs* out, void* stream) {
-  fh_status st = check_desc(desc, true);
-  if (st != FH_OK) return st;
-  if ((st = check_p(desc, p)) != FH_OK) return st;
-  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
-  if (!centroids) return fail(FH_ERR_ARG, "centroids must be non-NULL");
-  if ((st = check_tiles_args(desc, h, cluster_tokens, E_tiles, E_scales, out)) != FH_OK) return st;
-  fh::Workspace ws;
-  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+                            uint64_t seed, uint64_t step, const fh::Workspace& ws, const fh_outputs* out,
+                            void* stream) {
   const fh::HeadShape s = shape_of(desc);
   const fh::Sampling smp = sampling_of(mode, temperature, seed, step);
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = fh::launch_scores(s, h, centroids, smp, ws, nullptr, hs);
   if (e != hipSuccess) return hip_fail(e, "centroid scores launch");
   return select_and_probe(s, (int)p, h, cluster_tokens, E_tiles, E_scales, smp, ws, out, true, hs);
+}
+
+static fh_status check_forward_args(const fh_desc* desc, const void* h, const void* centroids,
+                                    const int32_t* cluster_tokens, const void* E_tiles, const void* E_scales, int64_t p,
+                                    int32_t mode, float temperature, const fh_outputs* out) {
+  fh_status st = check_desc(desc, true);
+  if (st != FH_OK) return st;
+  if ((st = check_p(desc, p)) != FH_OK) return st;
+  if ((st = check_sampling(mode, temperature)) != FH_OK) return st;
+  if (!centroids) return fail(FH_ERR_ARG, "centroids must be non-NULL");
+  return check_tiles_args(desc, h, cluster_tokens, E_tiles, E_scales, out);
+}
+
+fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
+                            const void* E_tiles, const void* E_scales, int64_t p, int32_t mode, float temperature,
+                            uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
+                            const fh_outputs* out, void* stream) {
+  fh_status st = check_forward_args(desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature, out);
+  if (st != FH_OK) return st;
+  fh::Workspace ws;
+  if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  return forward_on(desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature, seed, step, ws, out,
+                    stream);
 }
 
 fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* bytes) {

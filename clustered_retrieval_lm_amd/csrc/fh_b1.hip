@@ -11,7 +11,7 @@
 //   k_b1_stage2       every workgroup (one per CU) finds the same kept set from the keys,
 //                     streams its share of the kept clusters' tiles and writes its best
 //                     (key, token) candidate; the tiles of the clusters that are kept for
-//                     certain are requested before the rest of the selection is resolved;
+//                     certain are requested as soon as the boundary of the selection is known;
 //   k_finalize_parts  reduces the per-workgroup candidates to the token.
 //
 // This file is compiled once per row format (FH_B1_RF = RF_F32, RF_BF16, RF_INT4); each object
@@ -32,7 +32,7 @@ struct B1Params {
   const char* C;
   const uint16_t* c_scales;   // int4 centroids: their bf16 group scales
   int h_bf16, c, d, b, p;
-  int cpad;             // key slots (a multiple of kB1Threads); the ones past c hold -inf
+  int cpad;             // key slots (a multiple of kB1Threads); the ones past c hold NaN
   int sample;
   float tau;
   Rng rng;
@@ -52,9 +52,9 @@ struct B1Params {
 
 template <int RF, int CH>
 __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
-  // key slots past c: -inf is never kept (every real key is finite)
+  // key slots past c: quiet NaN, which every min, max and comparison of the selection ignores
   for (int i = a.c + blockIdx.x * kThreads + threadIdx.x; i < a.cpad; i += gridDim.x * kThreads)
-    a.keys[i] = -__builtin_huge_valf();
+    a.keys[i] = __uint_as_float(0x7FC00000u);
   const int lane = threadIdx.x & 63;
   const int wg = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nw = gridDim.x * 4;
@@ -90,28 +90,22 @@ __global__ __launch_bounds__(kThreads) void k_b1_scores(B1Params a) {
 __host__ __device__ __forceinline__ int b1_slots(int c) { return b1_key_slots(c) / kB1Threads; }
 
 constexpr int kS2MaxWords = 32768 / 64;
-constexpr int kSegCap = 128;               // middle keys one wave may hold
-constexpr int kS2RankMax = 64;             // keys one wave ranks exactly
-constexpr int kSubBits = 9;                // sub-histogram of the middle keys: 512 bins
-constexpr int kSubBins = 1 << kSubBits;
-constexpr int kSampBins = 128;             // histogram of wave 0's keys (the threshold sample)
+constexpr int kS2MaxCand = 64;             // keys the boundary bin may hold on the fast path
+constexpr int kItemMax = 256;              // (cluster, row group) items one workgroup may own
 
 struct S2Shared {
+  int hist[kSelBins];
   // Bitmaps over the clusters, wave-major: bit l of w[wave NS + s] is cluster s 1024 + 64 wave + l.
-  uint64_t words[kS2MaxWords];             // clusters with keys >= T_hi (kept for certain)
-  uint64_t bw[kS2MaxWords];                // the other kept clusters
-  uint64_t fullw[kS2MaxWords];             // all kept clusters (probe outputs; the general selection)
+  uint64_t words[kS2MaxWords];             // certain clusters (item mode, probe outputs) or all kept
+  uint64_t bw[kS2MaxWords];                // the kept clusters of the boundary bin
   int pref[kS2MaxWords];                   // kept clusters before id-ordered word i (probe ids)
-  __align__(16) int sub[kSubBins];         // middle keys per sub-bin of [T_lo, T_hi)
-  int samp[kSampBins];
-  float cx[16 * kSegCap];                  // middle keys, wave w's at [w kSegCap, (w + 1) kSegCap) ...
-  int cid[16 * kSegCap];                   // ... and their clusters
-  float cx2[kS2RankMax];                   // the middle keys of the boundary sub-bin ...
-  int cid2[kS2RankMax];                    // ... and their clusters
-  int nhi[16], nmid[16];
+  float wmx[16], wmn[16];
   int wtot[16];
-  float thr[2];                            // T_hi, T_lo
-  int ncand2;
+  int bnd[3];                              // boundary bin, keys above it, keys in it
+  int ncand, nitems;
+  float cx[kS2MaxCand];                    // the boundary bin's keys ...
+  int cid[kS2MaxCand];                     // ... and clusters
+  int items[kItemMax];                     // this workgroup's items: cluster << 8 | row group
   uint64_t wmax[16];
 };
 
@@ -185,72 +179,26 @@ __device__ __forceinline__ int kept_count_below(const uint64_t* words, int k) {
   return __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
 }
 
-// One wave: of the n <= 64 keys (cx, cid) in LDS, sets the `need` largest (ties to the smaller
-// cluster id) in the wave-major bitmap bw.  Exact: ranks by all pairwise comparisons.
-template <int NS>
-__device__ __forceinline__ void rank_keep(const float* cx, const int* cid, int n, int need, uint64_t* bw) {
-  const int lane = threadIdx.x & 63;
-  const bool act = lane < n;
-  const float xt = act ? cx[lane] : 0.f;
-  const int it = act ? cid[lane] : 0x7FFFFFFF;
-  int rank = 0;
-  for (int q = 0; q < n; ++q) {
-    const float xq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), q));
-    const int iq = __builtin_amdgcn_readlane(it, q);
-    rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
-  }
-  if (act && rank < need) wm_set<NS>(bw, it);
-}
-
-// One wave: in a histogram of 512 bins (lane l: bins [8 l, 8 l + 8)), the bin holding the
-// need-th largest item counted from the top (the bins above it hold fewer than need items,
-// with it at least need).  Returns (wave-uniform) the bin, the items above it and the items
-// in it; bin -1 if the histogram holds fewer than need items.
-__device__ __forceinline__ int3 wave_boundary_bin(const int* hist, int need) {
-  const int lane = threadIdx.x & 63;
-  const int4* hv = reinterpret_cast<const int4*>(hist) + 2 * lane;
-  const int4 v0 = hv[0], v1 = hv[1];
-  const int n[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  int t = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) t += n[j];
-  const int in = wave_incl_scan(t);
-  int cum = __builtin_amdgcn_readlane(in, 63) - in;        // items in the lanes above this one
-  const bool mine = cum < need && cum + t >= need;
-  int3 r = make_int3(-1, 0, 0);
-  if (mine) {
-#pragma unroll
-    for (int j = 7; j >= 0; --j) {
-      if (r.x < 0 && cum + n[j] >= need) r = make_int3(8 * lane + j, cum, n[j]);
-      cum += n[j];
-    }
-  }
-  const uint64_t who = __ballot(mine);
-  if (!who) return make_int3(-1, 0, 0);
-  const int L = __ffsll((unsigned long long)who) - 1;
-  return make_int3(__builtin_amdgcn_readlane(r.x, L), __builtin_amdgcn_readlane(r.y, L),
-                   __builtin_amdgcn_readlane(r.z, L));
-}
-
 // Selection and stage 2 for one hidden state in one kernel.  Every workgroup (1024 threads, one
 // per CU) holds the c keys in registers (slot s of thread t: cluster 1024 s + t) and finds the
-// same kept set:
-//  1. wave 0 estimates two thresholds from a 128-bin histogram of its own c/16 keys: about
-//     0.7 p keys of all lie at or above T_hi, and p with a margin at or above T_lo;
-//  2. one pass over the keys: those >= T_hi go into a bitmap (N_hi of them), those in
-//     [T_lo, T_hi) into per-wave LDS lists and a 512-bin histogram of their order-preserving
-//     codes (N_mid); if N_hi <= p <= N_hi + N_mid, the clusters >= T_hi are kept for certain
-//     and the tiles of this workgroup's share of them are requested at once;
-//  3. every wave finds the sub-bin of the 512 holding the (p - N_hi)-th middle key; the middle
-//     keys above it are kept, and wave 0 ranks the <= 64 in it exactly (key desc, id asc) while
-//     the other waves' tile loads are in flight.
-// Kept clusters are numbered 0 .. p-1: the certain ones by ascending id, then the others by
-// ascending id; workgroup g takes the numbers g, g + G, ...  Thresholds that miss (fewer than
-// p keys >= T_lo, more than p >= T_hi, a full list) or a boundary sub-bin with more than 64 keys
-// send the workgroup, block-uniformly and before any tile load, to the general selection
-// (select_regs), after which every kept cluster comes from one bitmap.  Each workgroup writes the packed maximum of its tokens to
-// part[g].  Probe outputs are indexed by the ascending rank of the cluster among all kept ones.
-// NS: key slots per thread, NR: tile rows per wave step.
+// same kept set, so no workgroup waits for another:
+//  * one float-linear 2048-bin histogram between the key min and max locates the bin b holding
+//    the p-th largest key; every key in a bin above b is kept for certain; wave 0 ranks the
+//    keys of bin b exactly (key desc, id asc) and keeps the first p - above of them;
+//  * the kept tiles are cut into items of NR rows, item (k, j) having the number
+//    h = k * gpp + j (gpp items per cluster).  With 256 workgroups (p >= 256), workgroup g takes
+//    the items with h % 256 == g: cluster k has an item there exactly when the thread holding
+//    its key (t = k % 1024) satisfies (g - t * gpp) % 256 < gpp, so those threads list the
+//    workgroup's certain items as soon as bin b is known, and the tile loads start before the
+//    boundary keys are ranked, with no block-wide numbering of the kept clusters.  The number
+//    of items per workgroup is about p gpp / 256, the kept clusters spreading over residues.
+//  * with fewer workgroups (p < 256), with more items than a workgroup can list, or after the
+//    general selection, the kept clusters are numbered 0 .. p-1 by ascending id (certain ones
+//    first) and workgroup g takes the numbers g, g + G, ... (ranks from the kept bitmap).
+// A boundary bin with more than kS2MaxCand keys (or all keys equal) sends the workgroup,
+// block-uniformly, to the general selection (select_regs).  Each workgroup writes the packed
+// maximum of its tokens to part[g].  Probe outputs are indexed by the ascending rank of the
+// cluster among all kept ones.  NS: key slots per thread, NR: tile rows per item.
 template <int RF, int CH, int NS, int NR>
 __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   constexpr int NT = kB1Threads, NWAVE = NT / 64;
@@ -263,113 +211,113 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   const int G = gridDim.x, me = blockIdx.x;
   const int c = a.c, p = a.p;
   const bool want = a.probe_out || a.logits_out || a.tokens_out;
-  // ---- keys (slots past c hold -inf)
+  const int gpp = (a.b + NR - 1) / NR;
+  // items per workgroup by hash need 256 workgroups and few enough items to list
+  bool itemized = G == kB1Workgroups && gpp <= kB1Workgroups &&                            // block-uniform
+                  p * gpp <= (kItemMax / 4) * kB1Workgroups;
+  // ---- keys; the slots past c hold NaN: ignored by min / max, never greater or equal
   float x[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) x[s] = a.keys[s * NT + tid];
+  for (int i = tid; i < kSelBins; i += NT) Q.hist[i] = 0;
   for (int i = tid; i < NWID; i += NT) Q.bw[i] = 0ull;
-  for (int i = tid; i < kSubBins; i += NT) Q.sub[i] = 0;
-  if (tid < kSampBins) Q.samp[tid] = 0;
-  if (tid == 0) Q.ncand2 = 0;
+  if (tid == 0) { Q.ncand = 0; Q.nitems = 0; }
+  float mx = x[0], mn = x[0];
+#pragma unroll
+  for (int s = 1; s < NS; ++s) { mx = fmaxf(mx, x[s]); mn = fminf(mn, x[s]); }
+  mx = wave_minmax_f32<true>(mx);
+  mn = wave_minmax_f32<false>(mn);
+  if (lane == 0) { Q.wmx[wave] = mx; Q.wmn[wave] = mn; }
   __syncthreads();                                                          // 1
-  // ---- 1. thresholds from wave 0's keys
-  if (wave == 0) {
-    float mx = -__builtin_huge_valf(), mn = __builtin_huge_valf();
-    int n0 = 0;                                          // wave 0's real keys (a closed form)
+  float hi = Q.wmx[0], lo = Q.wmn[0];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int left = c - s * NT;
-      n0 += left >= 64 ? 64 : (left > 0 ? left : 0);
-      if (s * NT + tid < c) { mx = fmaxf(mx, x[s]); mn = fminf(mn, x[s]); }
-    }
-    mx = wave_minmax_f32<true>(mx);
-    mn = wave_minmax_f32<false>(mn);
-    // sample ranks: k_hi ~ 0.7 p n0 / c; k_lo ~ 1.4 p n0 / c plus three standard deviations
-    const float ps = (float)p * (float)n0 / (float)c;
-    const int khi = (int)(0.7f * ps);
-    const int klo = (int)ceilf(1.4f * ps + 3.0f * sqrtf(ps) + 2.0f);
-    float thi = __builtin_huge_valf(), tlo = -3.4028235e38f;      // +inf / the lowest finite
-    if (mx > mn) {
-      const float scale = (float)kSampBins / (mx - mn);
+  for (int w = 1; w < NWAVE; ++w) { hi = fmaxf(hi, Q.wmx[w]); lo = fminf(lo, Q.wmn[w]); }
+  const float inv = (float)kSelBins / (hi - lo);
+  bool fast = hi > lo && inv > 0.f && inv < 3.0e38f;                        // block-uniform
+  const float off = -lo * inv;
+  int bins[NS];
+  if (fast) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        if (s * NT + tid < c) atomicAdd(&Q.samp[min((int)((x[s] - mn) * scale), kSampBins - 1)], 1);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // lane l: bins 2 l, 2 l + 1; counts from the top
-      const int h0 = Q.samp[2 * lane], h1 = Q.samp[2 * lane + 1];
-      const int in = wave_incl_scan(h0 + h1);
-      const int above = __builtin_amdgcn_readlane(in, 63) - in;   // sample keys in bins above 2 l + 1
-      // T_hi: the upper edge of the bin where the count from the top reaches khi (fewer than khi
-      // sample keys lie at or above it); T_lo: the lower edge of the bin where it reaches klo
-      if (khi >= 1) {
-        const bool in1 = above < khi && above + h1 >= khi;
-        const bool in0 = above + h1 < khi && above + h1 + h0 >= khi;
-        if (in1) thi = mn + (float)(2 * lane + 2) / scale;
-        if (in0) thi = mn + (float)(2 * lane + 1) / scale;
-      }
-      if (klo < n0) {
-        const bool in1 = above < klo && above + h1 >= klo;
-        const bool in0 = above + h1 < klo && above + h1 + h0 >= klo;
-        if (in1) tlo = mn + (float)(2 * lane + 1) / scale;
-        if (in0) tlo = mn + (float)(2 * lane) / scale;
-      }
-      thi = wave_minmax_f32<false>(thi);
-      tlo = wave_minmax_f32<true>(tlo);
+    for (int s = 0; s < NS; ++s) {                 // NaN padding lands in bin 0
+      bins[s] = (int)fminf(fmaxf(fmaf(x[s], inv, off), 0.f), (float)(kSelBins - 1));
+      atomicAdd(&Q.hist[bins[s]], 1);
     }
-    if (lane == 0) { Q.thr[0] = thi; Q.thr[1] = tlo; }
+    if (tid == 0 && NS * NT > c) atomicSub(&Q.hist[0], NS * NT - c);
   }
   __syncthreads();                                                          // 2
-  // ---- 2. one pass: certain keys into the bitmap, middle keys into lists and the sub-histogram
-  const float T_hi = Q.thr[0], T_lo = Q.thr[1];
-  const uint32_t olo = ord_key(T_lo);
-  const uint32_t span = ord_key(T_hi) - olo;
-  const int shift = span > (uint32_t)kSubBins ? 32 - __clz((int)((span - 1u) >> kSubBits)) : 0;
-  {
-    uint32_t wlo = 0u, whi = 0u;
-    int nh = 0, nm = 0;                                  // wave-uniform
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float v = x[s];
-      const bool hi = v >= T_hi;
-      const uint64_t mh = __ballot(hi);
-      put_lane(wlo, (uint32_t)mh, s);                                 // the ballot into lane s
-      put_lane(whi, (uint32_t)(mh >> 32), s);
-      nh += __popcll(mh);
-      const bool mid = v >= T_lo && !hi;                 // never the -inf padding
-      const uint64_t mm = __ballot(mid);
-      if (mm) {
-        if (mid) {
-          const int pos = nm + lane_prefix(mm);
-          if (pos < kSegCap) { Q.cx[wave * kSegCap + pos] = v; Q.cid[wave * kSegCap + pos] = s * NT + tid; }
-          atomicAdd(&Q.sub[(int)((ord_key(v) - olo) >> shift)], 1);
-        }
-        nm += __popcll(mm);
-      }
-    }
-    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-    if (lane == 0) { Q.nhi[wave] = nh; Q.nmid[wave] = nm; }
+  // ---- boundary bin: wave w scans bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
+  const int top = kSelBins - 1 - 128 * wave - 2 * lane;
+  int h_lo = 0, h_hi = 0, incl = 0;
+  if (fast) {
+    const int2 hh = *reinterpret_cast<const int2*>(&Q.hist[top - 1]);
+    h_lo = hh.x;
+    h_hi = hh.y;
+    incl = wave_incl_scan(h_lo + h_hi);
+    if (lane == 63) Q.wtot[wave] = incl;
   }
   __syncthreads();                                                          // 3
-  int n_hi = 0, n_mid = 0;
-  bool full = false;
+  if (fast) {
+    int before = 0, bw = -1;
 #pragma unroll
-  for (int w = 0; w < NWAVE; ++w) {
-    n_hi += Q.nhi[w];
-    n_mid += Q.nmid[w];
-    full = full || Q.nmid[w] > kSegCap;
+    for (int w = 0; w < NWAVE; ++w) {
+      const int t = Q.wtot[w];
+      if (bw < 0) {
+        if (before + t >= p) bw = w;
+        else before += t;
+      }
+    }
+    if (wave == bw) {                       // the slice holding the p-th key resolves it
+      const int cum = incl + before;
+      const int L = __ffsll((unsigned long long)__ballot(cum >= p)) - 1;
+      const int ex = cum - h_lo - h_hi;
+      if (lane == L) {
+        const bool upper = ex + h_hi >= p;
+        Q.bnd[0] = upper ? top : top - 1;
+        Q.bnd[1] = upper ? ex : ex + h_hi;
+        Q.bnd[2] = upper ? h_hi : h_lo;
+      }
+    }
   }
-  // the keys >= T_hi are kept for certain only if there are at most p of them and the middle
-  // keys complete them to at least p; the middle keys of the boundary sub-bin must fit one wave
-  bool fast = n_hi <= p && p <= n_hi + n_mid && !full;                   // block-uniform
-  int3 bb = make_int3(-1, 0, 0);
-  if (fast && p > n_hi) {
-    bb = wave_boundary_bin(Q.sub, p - n_hi);
-    fast = bb.x >= 0 && bb.z <= kS2RankMax;
+  __syncthreads();                                                          // 4
+  int b = 0, above = 0, inb = 0;
+  if (fast) {
+    b = Q.bnd[0];
+    above = Q.bnd[1];
+    inb = Q.bnd[2];
+    fast = b > 0 && inb <= kS2MaxCand;
   }
-  if (!fast) {
-    // the exact selection over all keys; every kept cluster goes to Q.bw
+  // ---- the keys of bin b compacted; this workgroup's items of the certain clusters listed by
+  //      the threads that hold them; the certain bitmap when it is needed
+  const int jme = (me - tid * gpp) & (kB1Workgroups - 1);     // this thread's row group, if < gpp
+  if (fast) {
+    const bool owner = itemized && jme < gpp;
+    uint32_t wlo = 0u, whi = 0u;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (owner && bins[s] > b) {
+        const int pos = atomicAdd(&Q.nitems, 1);
+        if (pos < kItemMax) Q.items[pos] = ((s * NT + tid) << 8) | jme;
+      }
+      if (want || !itemized) {
+        const uint64_t m = __ballot(bins[s] > b);
+        put_lane(wlo, (uint32_t)m, s);                               // the ballot into lane s
+        put_lane(whi, (uint32_t)(m >> 32), s);
+      }
+      const uint64_t e = __ballot(bins[s] == b);
+      if (e) {
+        int base = 0;
+        if (lane == __ffsll((unsigned long long)e) - 1) base = atomicAdd(&Q.ncand, __popcll(e));
+        base = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(base, __ffsll((unsigned long long)e) - 1));
+        const int pos = base + lane_prefix(e);
+        if (bins[s] == b && pos < kS2MaxCand) { Q.cx[pos] = x[s]; Q.cid[pos] = s * NT + tid; }
+      }
+    }
+    if ((want || !itemized) && lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+  }
+  __syncthreads();                                                          // 5
+  if (fast) fast = Q.ncand == inb;          // block-uniform
+  int n_def = above;                        // rank numbers below n_def index Q.words, the rest Q.bw
+  if (!fast) {                              // the general selection, then the full kept bitmap
     uint32_t u[KV][4];
     uint32_t Tu;
     int Tid;
@@ -384,83 +332,114 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
       put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
       put_lane(whi, (uint32_t)(m >> 32), s);
     }
-    if (lane < NS) Q.bw[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-    n_hi = 0;
+    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+    n_def = p;
+    itemized = false;
   }
-  const int n_def = n_hi;                   // numbers below n_def index Q.words, the rest Q.bw
-  const int n_my = me < p ? (p - me + G - 1) / G : 0;
-  const int gpp = (a.b + NR - 1) / NR;
-  const int nit = n_my * gpp;
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
-  // ---- this wave's first tile rows, when certain: resolved and requested now
+  const int n1 = itemized ? min(Q.nitems, kItemMax) : 0;   // certain items listed so far
+  // ---- this wave's first item, when certain: requested while wave 0 ranks the boundary keys
   RowGroup<RF, CH, NR> g0;
   int tl0 = 0, k0 = -1;
   HRaw<RF, CH> hraw;
   if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
-  if (fast && wave < nit) {
-    const int qi = wave / gpp, j0 = (wave - qi * gpp) * NR;
-    const int q = me + qi * G;
-    if (q < n_def) {
-      k0 = kept_rank_id<NS>(Q.words, q);
+  if (fast) {
+    int q0 = -1, j00 = 0;
+    if (itemized) {
+      if (wave < n1) { q0 = Q.items[wave] >> 8; j00 = (Q.items[wave] & 255) * NR; }
+    } else if (wave < (me < p ? (p - me + G - 1) / G : 0) * gpp) {
+      const int qi = wave / gpp, q = me + qi * G;
+      j00 = (wave - qi * gpp) * NR;
+      if (q < above) q0 = kept_rank_id<NS>(Q.words, q);
+    }
+    if (q0 >= 0) {
+      k0 = q0;
       const size_t row0 = (size_t)k0 * a.b;
-      tl0 = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
-      rows_load<RF, CH>(g0, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
+      tl0 = (lane < NR && j00 + lane < a.b) ? a.c2t[row0 + j00 + lane] : 0;
+      rows_load<RF, CH>(g0, a.tiles + row0 * rb, rb, j00, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
                         spr, lane);
     }
-  }
-  // ---- 3. the kept middle keys: above the boundary sub-bin, and the ranked ones in it
-  if (fast && p > n_hi) {
-    const int nmine = Q.nmid[wave];          // wave w marks its own list
-    for (int i = lane; i < nmine; i += 64) {
-      const float v = Q.cx[wave * kSegCap + i];
-      const int sb = (int)((ord_key(v) - olo) >> shift);
-      if (sb > bb.x) {
-        wm_set<NS>(Q.bw, Q.cid[wave * kSegCap + i]);
-      } else if (sb == bb.x) {
-        const int pos = atomicAdd(&Q.ncand2, 1);
-        Q.cx2[pos] = v;
-        Q.cid2[pos] = Q.cid[wave * kSegCap + i];
+    if (wave == 0) {                        // rank the boundary keys; keep the first p - above
+      const int n = inb;
+      const int need = p - above;
+      const bool act = lane < n;
+      const float xt = act ? Q.cx[lane] : 0.f;
+      const int it = act ? Q.cid[lane] : 0x7FFFFFFF;
+      int rank = 0;
+      for (int q = 0; q < n; ++q) {
+        const float xq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xt), q));
+        const int iq = __builtin_amdgcn_readlane(it, q);
+        rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
+      }
+      if (act && rank < need) {
+        wm_set<NS>(Q.bw, it);
+        const int jb = (me - it * gpp) & (kB1Workgroups - 1);
+        if (itemized && jb < gpp) {
+          const int pos = atomicAdd(&Q.nitems, 1);
+          if (pos < kItemMax) Q.items[pos] = (it << 8) | jb;
+        }
       }
     }
-    __syncthreads();
-    if (wave == 0) rank_keep<NS>(Q.cx2, Q.cid2, bb.z, p - n_hi - bb.y, Q.bw);
   }
-  __syncthreads();                                                          // 4
-  // ---- probe outputs: the full kept bitmap gives every cluster its ascending rank
-  const uint64_t* fw = Q.fullw;
-  if (want) {
-    for (int i = tid; i < NWID; i += NT) Q.fullw[i] = (n_def ? Q.words[i] : 0ull) | Q.bw[i];   // n_def = 0: words unused
-    __syncthreads();
-    if (me == 0 && a.probe_out) {
-      int tot2;
-      const int pc = tid < NWID ? __popcll(fw[wm_index<NS>(tid)]) : 0;
-      const int ex = block_scan(pc, Q.wtot, tot2);
-      if (tid < NWID) Q.pref[tid] = ex;
-      __syncthreads();
+  __syncthreads();                                                          // 6
+  const int n2 = itemized ? Q.nitems : 0;   // every item of this workgroup
+  if (itemized && n2 > kItemMax) {
+    // more items than the list holds: number the kept clusters instead (the certain bitmap from
+    // the keys again, the same bins, plus the kept boundary clusters); the early load is dropped
+    uint32_t wlo = 0u, whi = 0u;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const uint64_t m = fw[wave * NS + s];
-        if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
-      }
+    for (int s = 0; s < NS; ++s) {
+      const float v = a.keys[s * NT + tid];
+      const int bn = (int)fminf(fmaxf(fmaf(v, inv, off), 0.f), (float)(kSelBins - 1));
+      const uint64_t m = __ballot(bn > b && s * NT + tid < c);
+      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
+      put_lane(whi, (uint32_t)(m >> 32), s);
+    }
+    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+    itemized = false;
+    k0 = -1;
+    __syncthreads();
+  }
+  // ---- probe outputs: the kept clusters are Q.words | Q.bw (Q.bw is empty after the general
+  //      selection); workgroup 0 writes their ids in ascending order
+  if (want && me == 0 && a.probe_out) {
+    int tot;
+    const int pc = tid < NWID ? __popcll(Q.words[wm_index<NS>(tid)] | Q.bw[wm_index<NS>(tid)]) : 0;
+    const int ex = block_scan(pc, Q.wtot, tot);
+    if (tid < NWID) Q.pref[tid] = ex;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint64_t m = Q.words[wave * NS + s] | Q.bw[wave * NS + s];
+      if ((m >> lane) & 1ull) a.probe_out[Q.pref[s * NWAVE + wave] + lane_prefix(m)] = s * NT + tid;
     }
   }
-  // ---- stage 2 on this workgroup's clusters
+  // numbered mode: numbers below n_def are the ascending certain clusters (Q.words), the rest
+  // the kept clusters of the boundary bin (Q.bw)
+  const int nit = itemized ? n2 : (me < p ? (p - me + G - 1) / G : 0) * gpp;
+  // ---- stage 2 on this workgroup's items
   HRegs<RF, CH> hr;
   if constexpr (kEarlyH) unpack_h<RF, CH>(hr, hraw, a.h_bf16);
   else load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
   uint64_t bc = 0;
   for (int it = wave; it < nit; it += NWAVE) {
-    const int qi = it / gpp, j0 = (it - qi * gpp) * NR;
-    const int q = me + qi * G;
-    int k, tl;
+    int k, tl, j0;
     RowGroup<RF, CH, NR> g;
     if (it == wave && k0 >= 0) {
       k = k0;
       tl = tl0;
+      j0 = itemized ? (Q.items[it] & 255) * NR : (it - (it / gpp) * gpp) * NR;
       g = g0;
     } else {
-      k = q < n_def ? kept_rank_id<NS>(Q.words, q) : kept_rank_id<NS>(Q.bw, q - n_def);
+      if (itemized) {
+        k = Q.items[it] >> 8;
+        j0 = (Q.items[it] & 255) * NR;
+      } else {
+        const int qi = it / gpp, q = me + qi * G;
+        j0 = (it - qi * gpp) * NR;
+        k = q < n_def ? kept_rank_id<NS>(Q.words, q) : kept_rank_id<NS>(Q.bw, q - n_def);
+      }
       const size_t row0 = (size_t)k * a.b;
       tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
       rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
@@ -468,17 +447,19 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     }
     float z[NR];
     rows_dot<RF, CH>(g, hr, z);
-    const int qo = want ? kept_count_below<NS>(fw, k) : 0;
+    const int qo = want ? kept_count_below<NS>(Q.words, k) + kept_count_below<NS>(Q.bw, k) : 0;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int j = j0 + i;
       if (j < a.b) {
         const int t = __builtin_amdgcn_readlane(tl, i);
-        const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
-        const uint64_t cnd = pack_cand(key, (uint32_t)t);
-        bc = cnd > bc ? cnd : bc;
+        if (t >= 0) {                              // an empty slot (-1) is never chosen
+          const float key = make_key(z[i], a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
+          const uint64_t cnd = pack_cand(key, (uint32_t)t);
+          bc = cnd > bc ? cnd : bc;
+        }
         if (want && lane == 0) {
-          if (a.logits_out) a.logits_out[(size_t)qo * a.b + j] = z[i];
+          if (a.logits_out) a.logits_out[(size_t)qo * a.b + j] = t >= 0 ? z[i] : -__builtin_huge_valf();
           if (a.tokens_out) a.tokens_out[(size_t)qo * a.b + j] = t;
         }
       }
@@ -551,10 +532,20 @@ static void launch_scores_ch(const B1Params& a, hipStream_t st) {
   }
 }
 
+// Two tile rows per item only where the kernel still holds them in registers (longer rows
+// spill): fp32 rows up to 4 chunk slots, bf16 up to 3, int4 rows 1.
+template <int CH>
+constexpr bool kTwoRowsFit = kRF == RF_F32 ? CH <= 4 : kRF == RF_BF16 ? CH <= 3 : CH <= 1;
+
 template <int CH, int S>
 static void launch_stage2_s(const B1Params& a, int G, int nr, hipStream_t st) {
-  if (nr == 1) hipLaunchKernelGGL((k_b1_stage2<kRF, CH, S, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
-  else         hipLaunchKernelGGL((k_b1_stage2<kRF, CH, S, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
+  if constexpr (kTwoRowsFit<CH>) {
+    if (nr == 2) {
+      hipLaunchKernelGGL((k_b1_stage2<kRF, CH, S, 2>), dim3(G), dim3(kB1Threads), 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_b1_stage2<kRF, CH, S, 1>), dim3(G), dim3(kB1Threads), 0, st, a);
 }
 
 template <int CH>

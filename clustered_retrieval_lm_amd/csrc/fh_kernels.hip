@@ -398,10 +398,12 @@ __global__ __launch_bounds__(kThreads) void k_tiles_probe(TileParams a) {
       const int j = j0 + lane;
       if (lane < kRPI && j < a.b) {
         const int t = a.c2t[(size_t)k * a.b + j];
-        const float key = make_key(zi, a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
-        const uint64_t cnd = pack_cand(key, (uint32_t)t);
-        bc = cnd > bc ? cnd : bc;
-        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = zi;
+        if (t >= 0) {                              // an empty slot (-1) is never chosen
+          const float key = make_key(zi, a.sample, a.tau, a.rng, 0u, 1u, (uint32_t)t);
+          const uint64_t cnd = pack_cand(key, (uint32_t)t);
+          bc = cnd > bc ? cnd : bc;
+        }
+        if (a.logits_out) a.logits_out[(size_t)q * a.b + j] = t >= 0 ? zi : -__builtin_huge_valf();
         if (a.tokens_out) a.tokens_out[(size_t)q * a.b + j] = t;
       }
     }
@@ -479,10 +481,12 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
             const int t = lane_pick<kRPI>(tj, lane);
             const int j = j0 + lane;
             if (lane < kRPI && j < a.b) {
-              const float key = make_key(zi, SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
-              bc = pack_cand(key, (uint32_t)t);
+              if (t >= 0) {                          // an empty slot (-1) is never chosen
+                const float key = make_key(zi, SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+                bc = pack_cand(key, (uint32_t)t);
+              }
               const size_t o = ((size_t)r * a.p + lo) * a.b + j;
-              if (a.logits_out) a.logits_out[o] = zi;
+              if (a.logits_out) a.logits_out[o] = t >= 0 ? zi : -__builtin_huge_valf();
               if (a.tokens_out) a.tokens_out[o] = t;
             }
           }
@@ -587,8 +591,17 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams a) {
   const int ssz = a.src_bf16 ? 2 : 4;
   for (int row = gw; row < a.rows; row += nw) {
     const int t = a.c2t[row];
-    if (t < 0 || t >= a.V) {
+    if (t >= a.V) {
       if (lane == 0) atomicOr(a.bad, 1u);
+      continue;
+    }
+    if (t < 0) {                                   // an empty slot of a padded cluster: a zero row
+      if (lane == 0) atomicAdd(&a.counts[a.V], 1u);
+      const int rbytes = a.dst_fmt == RF_F32 ? 4 * a.d : a.dst_fmt == RF_BF16 ? 2 * a.d : a.d / 2;
+      uint32_t* dst = (uint32_t*)(a.tiles + (size_t)row * rbytes);
+      for (int e = lane; e < rbytes / 4; e += kWave) dst[e] = 0u;
+      if (a.dst_fmt == RF_INT4)
+        for (int gi = lane; gi < (a.d >> 7); gi += kWave) a.scales[(size_t)row * (a.d >> 7) + gi] = 0;
       continue;
     }
     if (lane == 0) atomicAdd(&a.counts[t], 1u);
@@ -647,9 +660,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_int4_rows(const uint16_t* sr
   }
 }
 
+// The tokens of C2T are exactly 0 .. n - 1, each once, n = V minus the empty slots (counts[V]).
 __global__ void k_check_counts(const uint32_t* counts, int V, uint32_t* bad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < V && counts[i] != 1u) atomicOr(bad, 2u);
+  const int n = V - (int)counts[V];
+  if (i < V && counts[i] != (i < n ? 1u : 0u)) atomicOr(bad, 2u);
 }
 
 // ------------------------------------------------------------------ cluster centroids
@@ -687,8 +702,14 @@ __global__ __launch_bounds__(kThreads) void k_centroids(CentroidParams a) {
     return a.src_bf16 ? (double)bf16_to_f32(*(const uint16_t*)src) : (double)*(const float*)src;
   };
   const int32_t* rows = a.c2t + (size_t)k * a.b;
+  int nmem = 0;                          // members: the slots that are not empty (-1)
+  for (int j = 0; j < a.b; ++j) nmem += rows[j] >= 0 ? 1 : 0;
   if (a.unit) {
     for (int j = 0; j < a.b; ++j) {
+      if (rows[j] < 0) {
+        if (tid == 0) inv_norm[j] = 0.0;
+        continue;
+      }
       double ss = 0.0;
       for (int e = tid; e < a.d; e += kThreads) { const double v = val(rows[j], e); ss += v * v; }
       for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, kWave);
@@ -712,9 +733,12 @@ __global__ __launch_bounds__(kThreads) void k_centroids(CentroidParams a) {
     }
     for (int e = tid; e < a.d; e += kThreads) {
       double sum = 0.0;
-      for (int j = 0; j < a.b; ++j) sum += a.unit ? val(rows[j], e) * inv_norm[j] : val(rows[j], e);
+      for (int j = 0; j < a.b; ++j) {
+        if (rows[j] < 0) continue;
+        sum += a.unit ? val(rows[j], e) * inv_norm[j] : val(rows[j], e);
+      }
       if (a.unit && pass == 0) { nsq += sum * sum; continue; }
-      const double m = a.unit ? sum * scale : sum / (double)a.b;
+      const double m = a.unit ? sum * scale : (nmem ? sum / (double)nmem : 0.0);
       const size_t o = (size_t)k * a.d + e;
       if (a.dst_bf16) ((uint16_t*)a.out)[o] = f64_to_bf16_rne(m);
       else ((float*)a.out)[o] = (float)m;

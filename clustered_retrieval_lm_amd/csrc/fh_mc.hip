@@ -361,7 +361,8 @@ __global__ __launch_bounds__(kMcThreads) void k_mc_expand(const float* z, const 
     const double Ak = A[rk];
     double est = 0.0;
     if (Ak > 0.0) est = exp((double)z[(size_t)r * V + slot] / tau - M[rk]) * Ak * inv_n;
-    out[(size_t)r * V + c2t[slot]] = est;
+    const int t = c2t[slot];
+    if (t >= 0) out[(size_t)r * V + t] = est;      // empty slots of padded clusters are skipped
     // positive doubles order like their bit patterns: the smallest has the largest complement
     if (est > 0.0) key = ~(uint64_t)__double_as_longlong(est);
   }

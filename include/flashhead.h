@@ -116,9 +116,13 @@ fh_status flashhead_workspace_bytes(const fh_desc* desc, int64_t p, size_t* byte
  *   E_scales       device out, INT4_G128 only: bf16 [c][b][d/128], s = bf16(amax / 7) of each
  *                  group of 128 elements (s = 0 and q = 0 for an all-zero group); else NULL
  * The low-bit format is this library's reading of the paper's selective quantization
- * (Section 3.2, "Quantization note"; Table 5).  Checks that C2T is a permutation:
- * FH_ERR_ARG if it is not.  This call allocates a small device buffer and synchronises
- * `stream`.
+ * (Section 3.2, "Quantization note"; Table 5).
+ * Unequal clusters (the ablation of Sections 3.1 and 4.5, Table 6): C2T keeps its dense
+ * [c][b] shape with b = the largest cluster and -1 in the empty slots of smaller clusters
+ * (desc->V = c b slots); an empty slot gets a zero row.  Checks that the entries other than -1
+ * are the tokens 0 .. n-1 once each (n = the slots that are not empty; with equal clusters a
+ * permutation of [0, V)): FH_ERR_ARG if not.  This call allocates a small device buffer and
+ * synchronises `stream`.
  */
 fh_status flashhead_pack(const fh_desc* desc, int32_t src_dtype, const void* E,
                          const int32_t* cluster_tokens, void* E_tiles, void* E_scales,
@@ -165,8 +169,9 @@ fh_status flashhead_centroids_bytes(const fh_desc* desc, size_t* bytes);
 /*
  * Offline centroids of a given clustering (Section 3.1, "Centroid matrix").
  *   E              device, [V][d] token-major embeddings of dtype src_dtype (F32 | BF16)
- *   cluster_tokens device, int32 [c][b]: C2T
- *   unit           0: C[k] = mean of the b rows of cluster k;
+ *   cluster_tokens device, int32 [c][b]: C2T (entries -1: empty slots of a padded C2T, see
+ *                  flashhead_pack, which are not members; a cluster without members gets 0)
+ *   unit           0: C[k] = mean of the member rows of cluster k;
  *                  1: C[k] = normalise(sum of the normalised rows), the unit centroid the
  *                     paper stores (a zero row or sum contributes / gives 0)
  *   centroids      device out, [c][d] in desc->c_dtype (layout: flashhead_centroids_bytes)
@@ -245,6 +250,8 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
  *                  stages; seed / step key the Philox draws
  *   workspace      device, >= flashhead_workspace_bytes(desc, p)
  *   out            host struct of device pointers
+ * An empty slot of a padded C2T (entry -1, see flashhead_pack) gathers nothing: it is never the
+ * token, and out->probe_tokens / probe_logits report it as -1 / -inf.
  * Limits of this build: d % 8 == 0, d <= 4096 (bf16 rows), <= 2048 (f32 rows), d % 128 == 0
  * and d <= 8192 (int4 rows); c <= 32768; 1 <= b <= 256; V < 2^31; B <= 65535.
  */
@@ -272,6 +279,8 @@ fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* byt
  *   clip           0 | 1
  *   workspace      device, >= flashhead_mc_marginal_workspace_bytes(desc)
  *   out            device double [B][V], indexed by vocabulary id
+ * It needs equal clusters (a C2T without empty slots); the empty slots of a padded C2T are
+ * never written in `out`, but the estimate does not exclude them.
  * The logits s and z are computed with fp32 accumulation (s as flashhead_centroid_scores;
  * z over the whole tile array, as flashhead_dense_forward for bf16 / fp32 tiles and as
  * flashhead_probe_logits for int4 tiles); the softmax statistics and the average are fp64,

@@ -19,7 +19,10 @@ Readings fixed here (the page is silent on them):
   * tau applies to both stages;
   * ties: the larger key wins, then the smaller cluster id (probe selection)
     or the smaller vocabulary id (token);
-  * probe_ids are reported in ascending cluster id, probe logits in that order.
+  * probe_ids are reported in ascending cluster id, probe logits in that order;
+  * unequal clusters (the ablation of Sections 3.1 and 4.5) keep the dense C2T padded to the
+    largest cluster: an entry -1 is an empty slot, which gathers nothing -- its logit is
+    reported as -inf and its token as -1, and it is never chosen.
 
 All arithmetic is fp64 on exactly decoded inputs: products of bf16 / fp32 /
 int4-dequantised values are exact in fp64.
@@ -65,8 +68,11 @@ class PackedTiles:
 
 
 def pack_tiles(E: np.ndarray, e_dtype: str, C2T: np.ndarray, dst: str) -> PackedTiles:
-    """Gather E's rows into cluster-major tiles, optionally quantised to int4."""
-    rows = np.asarray(E)[np.asarray(C2T, dtype=np.int64)]      # [c][b][d]
+    """Gather E's rows into cluster-major tiles, optionally quantised to int4; an empty slot
+    (C2T entry -1) gets a zero row."""
+    C2T = np.asarray(C2T, dtype=np.int64)
+    rows = np.asarray(E)[np.maximum(C2T, 0)]                   # [c][b][d]
+    rows[C2T < 0] = 0
     if dst == e_dtype:
         return PackedTiles(dst, np.ascontiguousarray(rows))
     vals = decode(rows, e_dtype)
@@ -156,15 +162,17 @@ def forward(h: np.ndarray, h_dtype: str, C: np.ndarray, c_dtype: str, C2T: np.nd
             key1[r] = s[r] / tau + philox.gumbel(philox.uniform(seed, r, step, 0, ks))
         order1[r] = np.lexsort((ks, -key1[r]))
         probe[r] = np.sort(order1[r][:p])
-        # stage 2: logits of the gathered tokens
+        # stage 2: logits of the gathered tokens (empty slots of padded clusters gather nothing)
         T = tiles.values(probe[r])                             # [p][b][d]
-        z[r] = T @ H[r]
-        absz[r] = np.abs(T) @ np.abs(H[r])
         toks[r] = C2T[probe[r]]
+        real = toks[r] >= 0
+        z[r] = np.where(real, T @ H[r], -np.inf)
+        absz[r] = np.where(real, np.abs(T) @ np.abs(H[r]), 0.0)
         if mode == "greedy":
             key2[r] = z[r]
         else:
-            key2[r] = z[r] / tau + philox.gumbel(philox.uniform(seed, r, step, 1, toks[r]))
+            key2[r] = -np.inf
+            key2[r][real] = z[r][real] / tau + philox.gumbel(philox.uniform(seed, r, step, 1, toks[r][real]))
         flat_t = toks[r].reshape(-1)
         order2[r] = np.lexsort((flat_t, -key2[r].reshape(-1)))
         token[r] = flat_t[order2[r][0]]

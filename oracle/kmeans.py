@@ -119,6 +119,7 @@ def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str, unit: boo
 
     unit=False: the mean of each cluster's raw rows (float64 values);
     unit=True:  the normalised sum of the members' normalised rows (Section 3.1's c_k).
+    Entries -1 of C2T (empty slots of a padded clusters matrix) are not members.
     out_dtype "int4": the stage-1 quantisation of the paper's selective quantisation
     (Section 4.5, Table 5): the bf16 centroids, quantised per group of 128 like the int4
     token rows; returns the pair (nibbles [c][d/2], bf16 scale bits [c][d/128]).
@@ -129,14 +130,16 @@ def centroids_from_c2t(E: np.ndarray, C2T: np.ndarray, out_dtype: str, unit: boo
     c, b = C2T.shape
     cent = np.empty((c, E.shape[1]), dtype=np.float64)
     for lo in range(0, c, _ROW_BLOCK):
-        rows = np.asarray(E[C2T[lo:lo + _ROW_BLOCK]], dtype=np.float64)
+        blk = C2T[lo:lo + _ROW_BLOCK]
+        member = (blk >= 0)[..., None]
+        rows = np.where(member, np.asarray(E[np.maximum(blk, 0)], dtype=np.float64), 0.0)
         if unit:
             n = np.linalg.norm(rows, axis=2, keepdims=True)
             sums = np.where(n > 0, rows / np.where(n > 0, n, 1.0), 0.0).sum(axis=1)
             sn = np.linalg.norm(sums, axis=1, keepdims=True)
             cent[lo:lo + _ROW_BLOCK] = np.where(sn > 0, sums / np.where(sn > 0, sn, 1.0), 0.0)
         else:
-            cent[lo:lo + _ROW_BLOCK] = rows.mean(axis=1)
+            cent[lo:lo + _ROW_BLOCK] = rows.sum(axis=1) / member.sum(axis=1)
     return codecs.round_to_bf16(cent) if out_dtype == "bf16" else codecs.round_to_f32(cent)
 
 

@@ -77,14 +77,16 @@ def L_stage1(B: int, h_dtype: str, c_dtype: str, d: int) -> int:
 
 
 def key_bound(z: np.ndarray, A: np.ndarray, L: int, sample: bool, tau: float, G=None) -> np.ndarray:
-    """Bound on |GPU key - exact key| for logits z with absolute sums A."""
+    """Bound on |GPU key - exact key| for logits z with absolute sums A (0 for the -inf logit of
+    an empty slot, which both sides report exactly)."""
     e = gamma(L) * A
     if not sample:
         return e
-    x = np.abs(z) / tau
-    g = np.abs(G)
+    fin = np.isfinite(z)
+    x = np.where(fin, np.abs(z), 0.0) / tau
+    g = np.where(fin, np.abs(G), 0.0)
     # z/tau rounded, G from two fp32 logs (taken as within 2^-20 (1 + |G|)), the sum rounded
-    return e / tau + U * x + 2.0 ** -20 * (1.0 + g) + U * (x + g) * 1.001 + 1e-30
+    return np.where(fin, e / tau + U * x + 2.0 ** -20 * (1.0 + g) + U * (x + g) * 1.001 + 1e-30, 0.0)
 
 
 @functools.lru_cache(maxsize=None)
@@ -179,7 +181,7 @@ def stage1_bounds(ref: ohead.HeadResult, r: int, L1: int, sample: bool, tau: flo
 
 def stage2_bounds(ref: ohead.HeadResult, r: int, L2: int, sample: bool, tau: float, seed: int, step: int):
     flat_tok = ref.tokens[r].reshape(-1)
-    G2 = philox.gumbel(philox.uniform(seed, r, step, 1, flat_tok)) if sample else None
+    G2 = philox.gumbel(philox.uniform(seed, r, step, 1, np.maximum(flat_tok, 0))) if sample else None
     return key_bound(ref.z[r].reshape(-1), ref.absz[r].reshape(-1), L2, sample, tau, G2)
 
 
@@ -199,7 +201,8 @@ def row_flags(ref: ohead.HeadResult, r: int, p: int, L1: int, L2: int, sample: b
     flat_key = ref.key2[r].reshape(-1)
     e2 = stage2_bounds(ref, r, L2, sample, tau, seed, step)
     o2 = ref.order2[r]
-    ft = bool(flat_key.size > 1 and (flat_key[o2[0]] - flat_key[o2[1]] <= e2[o2[0]] + e2[o2[1]]))
+    ft = bool(flat_key.size > 1 and np.isfinite(flat_key[o2[1]])
+              and (flat_key[o2[0]] - flat_key[o2[1]] <= e2[o2[0]] + e2[o2[1]]))
     return False, ft
 
 
@@ -239,6 +242,9 @@ def compare_row(ref: ohead.HeadResult, r: int, got_ids: np.ndarray, got_z: np.nd
     common, gi, oi = np.intersect1d(got_ids, ref.probe_ids[r], return_indices=True)
     zg = np.asarray(got_z, dtype=np.float64)[gi]
     zo = ref.z[r][oi]
+    empty = ref.tokens[r][oi] < 0                 # empty slots of padded clusters: -inf on both sides
+    assert np.all(zg[empty] == -np.inf), f"row {r}: an empty slot's logit is not -inf"
+    zg, zo = np.where(empty, 0.0, zg), np.where(empty, 0.0, zo)
     dz = np.abs(zg - zo)
     rep.max_logit_err = max(rep.max_logit_err, float(dz.max()) if dz.size else 0.0)
     if fp32_inputs:
@@ -256,10 +262,11 @@ def compare_row(ref: ohead.HeadResult, r: int, got_ids: np.ndarray, got_z: np.nd
     if not sample:
         assert int(got_token) == int(gt[np.lexsort((gt, -gz))[0]]), f"row {r}: token is not the largest gathered logit"
     else:
-        g = philox.gumbel(philox.uniform(seed, r, step, 1, gt))
+        g = philox.gumbel(philox.uniform(seed, r, step, 1, np.maximum(gt, 0)))
         x = gz / tau
-        kk = x + g
-        eb = U * np.abs(x) + 2.0 ** -20 * (1.0 + np.abs(g)) + U * (np.abs(x) + np.abs(g)) * 1.001
+        kk = np.where(gt >= 0, x + g, -np.inf)
+        eb = np.where(gt >= 0, U * np.abs(np.where(gt >= 0, x, 0.0)) + 2.0 ** -20 * (1.0 + np.abs(g))
+                      + U * (np.abs(np.where(gt >= 0, x, 0.0)) + np.abs(g)) * 1.001, 0.0)
         assert kk[pos[0]] + eb[pos[0]] >= np.max(kk - eb), f"row {r}: token is not the Gumbel-max of its logits"
     if flagged:
         rep.flag_token += 1

@@ -151,3 +151,37 @@ def make_small(d: int, V: int, c: int, B: int, seed: int, sigma_c: float = 1.0,
     wl = Workload(f"small_{d}_{V}_{c}", d=d, V=V, c=c, B=B, p=1, sigma_c=sigma_c,
                   sigma_n=sigma_n, dtype=dtype, e_pack=dtype, temperatures=(1.0,))
     return HeadData(wl=wl, E=E, h=to_storage(h, dtype), latent=lat[perm])
+
+
+def make_unequal_clusters(latent: np.ndarray, c: int, seed: int, sigma: float = 0.5):
+    """An unequal clustering of the V tokens into c clusters: the input of the equal- versus
+    unequal-cluster ablation (FlashHead paper, Section 4.5, Table 6).
+
+    Cluster sizes are drawn as max(1, rne(m exp(sigma z - sigma^2 / 2))), z ~ N(0, 1), m = V / c
+    (a lognormal spread around the equal size), then single tokens are added to or taken from
+    random clusters (never below 1) until they sum to V.  The tokens, ordered by latent label
+    and then id, are cut into consecutive runs of those sizes, so a cluster holds tokens of one
+    or a few neighbouring latent groups.  Returns (C2T [c][b_max] int32 with each row's tokens
+    in ascending id followed by -1 padding, sizes [c] int64).
+    """
+    latent = np.asarray(latent)
+    V = latent.size
+    rng = np.random.default_rng(seed)
+    m = V / c
+    sizes = np.maximum(1, np.rint(m * np.exp(sigma * rng.standard_normal(c) - sigma * sigma / 2))).astype(np.int64)
+    diff = int(V - sizes.sum())
+    while diff != 0:
+        k = int(rng.integers(c))
+        if diff > 0:
+            sizes[k] += 1
+            diff -= 1
+        elif sizes[k] > 1:
+            sizes[k] -= 1
+            diff += 1
+    order = np.lexsort((np.arange(V), latent))
+    C2T = np.full((c, int(sizes.max())), -1, dtype=np.int32)
+    start = 0
+    for k in range(c):
+        C2T[k, :sizes[k]] = np.sort(order[start:start + sizes[k]])
+        start += sizes[k]
+    return C2T, sizes
