@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/flashhead.h"
@@ -109,6 +110,31 @@ fh::HeadShape shape_of(const fh_desc* d) {
 
 fh::Sampling sampling_of(int32_t mode, float tau, uint64_t seed, uint64_t step) {
   return fh::Sampling{mode == FH_SAMPLE ? 1 : 0, tau, seed, step};
+}
+
+// Scratch of flashhead_forward_noalloc: a workspace the library owns, one copy per device, held
+// until the process ends.  The array's name is a host-side stand-in; kernels get the device
+// address that hipGetSymbolAddress returns for the current device (kept in g_scratch_ptr).
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fh_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FH_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FH_OK;
 }
 
 }  // namespace
@@ -334,7 +360,7 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
                           sampling_of(mode, temperature, seed, step), ws, out, false, (hipStream_t)stream);
 }
 
-// The forward path of flashhead_forward on a carved workspace.
+// The forward path of flashhead_forward and flashhead_forward_noalloc on a carved workspace.
 static fh_status forward_on(const fh_desc* desc, const void* h, const void* centroids, const int32_t* cluster_tokens,
                             const void* E_tiles, const void* E_scales, int64_t p, int32_t mode, float temperature,
                             uint64_t seed, uint64_t step, const fh::Workspace& ws, const fh_outputs* out,
@@ -366,6 +392,23 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
   if (st != FH_OK) return st;
   fh::Workspace ws;
   if ((st = check_ws(desc, p, workspace, workspace_bytes, &ws)) != FH_OK) return st;
+  return forward_on(desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature, seed, step, ws, out,
+                    stream);
+}
+
+fh_status flashhead_forward_noalloc(const fh_desc* desc, const void* h, const void* centroids,
+                                    const int32_t* cluster_tokens, const void* E_tiles, const void* E_scales,
+                                    int64_t p, int32_t mode, float temperature, uint64_t seed, uint64_t step,
+                                    const fh_outputs* out, void* stream) {
+  fh_status st = check_forward_args(desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature, out);
+  if (st != FH_OK) return st;
+  const size_t need = fh::carve_workspace(nullptr, (int)desc->B, (int)desc->c, (int)p).bytes;
+  if (need > kStaticScratchBytes)
+    return fail(FH_ERR_UNSUPPORTED, "this head needs %zu bytes of workspace; the static scratch holds %zu "
+                "(use flashhead_forward with a caller workspace)", need, kStaticScratchBytes);
+  void* base = nullptr;
+  if ((st = scratch_of_current_device(&base)) != FH_OK) return st;
+  const fh::Workspace ws = fh::carve_workspace(base, (int)desc->B, (int)desc->c, (int)p);
   return forward_on(desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature, seed, step, ws, out,
                     stream);
 }

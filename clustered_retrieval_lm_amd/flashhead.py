@@ -77,6 +77,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "flashhead_mc_marginal": ([D, vp, vp, vp, vp, vp, i64, f32, u64, i64, i32, vp, sz, vp, vp], ctypes.c_int),
         "flashhead_dense_workspace_bytes": ([D, ctypes.POINTER(sz)], ctypes.c_int),
         "flashhead_dense_forward": ([D, vp, vp, i32, f32, u64, u64, vp, sz, vp, vp, vp], ctypes.c_int),
+        "flashhead_forward_noalloc": ([D, vp, vp, vp, vp, vp, i64, i32, f32, u64, u64, O, vp], ctypes.c_int),
         "flashhead_philox_words": ([u64, ctypes.c_uint32, u64, ctypes.c_uint32, ctypes.c_uint32, i64, vp, vp, vp],
                                    ctypes.c_int),
     }
@@ -253,3 +254,13 @@ def flashhead_philox_words(seed, row, step, rng_stream, n0, count, words_out=Non
                            stream=None) -> None:
     _check(load_library().flashhead_philox_words(int(seed), int(row), int(step), int(rng_stream), int(n0),
                                                  int(count), _ptr(words_out), _ptr(gumbel_out), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 4 << 20     # the static scratch of flashhead_forward_noalloc (include/flashhead.h)
+
+
+def flashhead_forward_noalloc(desc: fh_desc, h, centroids, cluster_tokens, E_tiles, E_scales, p, mode, temperature,
+                              seed, step, out: fh_outputs, stream=None) -> None:
+    _check(load_library().flashhead_forward_noalloc(
+        ctypes.byref(desc), _ptr(h), _ptr(centroids), _ptr(cluster_tokens), _ptr(E_tiles), _ptr(E_scales), int(p),
+        _mode(mode), float(temperature), int(seed), int(step), ctypes.byref(out), _stream(stream)))

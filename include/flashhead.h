@@ -261,6 +261,23 @@ fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* cent
                             uint64_t seed, uint64_t step, void* workspace, size_t workspace_bytes,
                             const fh_outputs* out, void* stream);
 
+/*
+ * flashhead_forward without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * workspace is a static scratch array inside the library, one per device, of 4 MiB (4194304
+ * bytes), held until the process ends.  Arguments,
+ * results and errors as for flashhead_forward; a head whose workspace
+ * (flashhead_workspace_bytes) exceeds the scratch returns FH_ERR_UNSUPPORTED.  Every call on a
+ * device shares that device's scratch: calls that overlap in time on one device (other streams,
+ * other threads) race and give undefined results; calls ordered on one stream are safe.  The
+ * first call on a device looks up the scratch's device address (no allocation); nothing here
+ * calls hipMalloc or hipFree.
+ */
+fh_status flashhead_forward_noalloc(const fh_desc* desc, const void* h, const void* centroids,
+                                    const int32_t* cluster_tokens, const void* E_tiles,
+                                    const void* E_scales, int64_t p, int32_t mode, float temperature,
+                                    uint64_t seed, uint64_t step, const fh_outputs* out, void* stream);
+
 /* Workspace size (bytes, device memory) for flashhead_mc_marginal. */
 fh_status flashhead_mc_marginal_workspace_bytes(const fh_desc* desc, size_t* bytes);
 
