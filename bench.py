@@ -28,6 +28,7 @@ import argparse
 import ctypes
 import json
 import os
+import re
 import sys
 import time
 
@@ -85,13 +86,14 @@ def measured_traffic(workload: str, kernels) -> "int | None":
         if line.startswith("source_sha256:"):
             sha = line.split(":", 1)[1].strip()
         elif line.startswith("kernel:"):
-            f = line.split()
-            found[f[1]] = int(f[-1].split("=")[1])
+            m = re.match(r"kernel:\s*(?:void\s+)?(\S+?)(?:<[^>]*>)?(?:\([^)]*\))?\s+dispatches=.*?traffic_bytes=(\d+)", line)
+            if m:
+                found[m.group(1)] = int(m.group(2))
     if sha != source_sha256():
         return None
     total = 0
     for k in kernels:
-        hits = [v for n, v in found.items() if n.split("<")[0] == k]
+        hits = [v for n, v in found.items() if n == k or n.split("::")[-1] == k.split("::")[-1]]
         if len(hits) != 1:
             return None
         total += hits[0]

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     uint32_t wlo = 0u, whi = 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float v = a.keys[s * NT + tid];
+      const float v = NS < 32 ? x[s] : a.keys[s * NT + tid];     // 32 slots: not kept in registers
       const uint64_t m = __ballot(v > T) | __ballot(v == T && s * NT + tid <= Tid);
       put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
       put_lane(whi, (uint32_t)(m >> 32), s);
@@ -388,9 +388,11 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     // more items than the list holds: number the kept clusters instead (the certain bitmap from
     // the keys again, the same bins, plus the kept boundary clusters); the early load is dropped
     uint32_t wlo = 0u, whi = 0u;
+    const float* kb = a.keys;
+    asm volatile("" : "+s"(kb));            // fresh addresses here: none are kept from the first reads
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const float v = a.keys[s * NT + tid];
+      const float v = kb[s * NT + tid];
       const int bn = (int)fminf(fmaxf(fmaf(v, inv, off), 0.f), (float)(kSelBins - 1));
       const uint64_t m = __ballot(bn > b && s * NT + tid < c);
       put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s

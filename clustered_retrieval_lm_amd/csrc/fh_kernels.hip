@@ -11,6 +11,8 @@
 //
 // Method: "FlashHead: Efficient Drop-In Replacement for the Classification Head in
 // Language Model Inference", Section 3.2 (two-stage retrieval, dense C2T).
+#include <atomic>
+
 #include "fh_device.h"
 #include "fh_internal.h"
 #include "fh_rows.h"
@@ -82,17 +84,20 @@ __global__ __launch_bounds__(kThreads) void k_scores_gemv(ScoreParams a) {
 // (lane l: row l % 16, k = 8 (l / 16) .. +7), B = 16 rows of H (same lane map),
 // D lane l: column n = l % 16, rows m = 4 (l / 16) + i.
 //
-// A workgroup of kMfmaWaves waves owns kMfmaMT 16-row tiles of M at a time (32 rows) and NT
-// 16-row tiles of H (up to 64 rows); its waves split K: wave w takes the K-steps (32 columns
-// each) w, w + 8, ...  A wave issues the loads of up to GS of its K-steps (the whole range at
-// d = 1024 and NT = 4) before any MFMA, so a tile costs about one memory round trip.  With
+// A workgroup of kMfmaWaves waves owns MT 16-row tiles of M at a time (32 to 64 rows) and NT
+// 16-row tiles of H (up to 64 rows); its waves split K by pairs of K-steps (32 columns each):
+// wave w takes the steps 2w, 2w + 1, 2w + 16, 2w + 17, ...  A wave issues the loads of up to
+// GS of its K-steps (the whole range at d = 1024 and NT = 4) before any MFMA, so a tile costs
+// about one memory round trip.  With
 // NACC > 1 a wave rotates NACC accumulators per tile over its K-steps, shortening the rounding
 // chain, and sums them by a tree at the end; the partial tiles of the 8 waves are summed in
 // LDS by a fixed 3-level tree.  Roundings on the path of one product: <= 6 per MFMA (32 exact
 // bf16 products and the accumulator, a tree of depth 6) times ceil(steps per wave / NACC),
-// + log2(NACC), + 3.
+// + log2(NACC), + 3; a wave takes at most 2 ceil(d / 512) steps.
 constexpr int kMfmaWaves = 8;
-constexpr int kMfmaMT = 2;
+// Every workgroup reads all of its H rows once per group: a CU streams about 24 KB/us, so the
+// launch takes the smallest MT (2..4) whose groups fit on the CUs in one round.
+constexpr int kMfmaMaxMT = 4;
 constexpr int kMfmaThreads = kMfmaWaves * 64;
 
 enum { EPI_KEYS = 0, EPI_ARGMAX = 1 };
@@ -114,10 +119,11 @@ struct MfmaParams {
   float* logits;      // EPI_ARGMAX: [B][rows], may be null
 };
 
-template <int NT, int EPI>
+template <int NT, int MT, int EPI>
 __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
-  constexpr int MT = kMfmaMT, NW = kMfmaWaves;
-  constexpr int GS = NT >= 3 ? 4 : 8;               // K-steps per load group (register budget)
+  constexpr int NW = kMfmaWaves;
+  // K-steps per load group (register budget: the group's loads, MT + NT 16-byte words a step)
+  constexpr int GS = MT + NT <= 3 ? 8 : MT + NT <= 6 ? 4 : 2;
   constexpr int NACC = NT == 1 ? 4 : NT == 2 ? 2 : 1;
   __shared__ f32x4_t red[NW][MT * NT][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -125,6 +131,9 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
   const int kq = (lane >> 4) * 8;
   const int nsteps = a.d / 32;
   const int ngroups = (a.rows + 16 * MT - 1) / (16 * MT);
+  // workgroups start their K range at different even steps, so the ones running together read
+  // different lines of H first
+  const int rot = (nsteps & 1) ? 0 : (2 * (int)(blockIdx.x % 8u) * ((nsteps + 15) / 16)) % nsteps;
   const uint16_t* hp[NT];
   bool hv[NT];
 #pragma unroll
@@ -134,7 +143,9 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
     hp[t] = a.H + (size_t)(hv[t] ? n : 0) * a.d + kq;
   }
   const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-  uint64_t bc = 0;
+  uint64_t bc[NT];                                   // EPI_ARGMAX: best candidate per H tile
+#pragma unroll
+  for (int t = 0; t < NT; ++t) bc[t] = 0;
   for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
     const int m0 = grp * 16 * MT;
     const uint16_t* mp[MT];
@@ -152,12 +163,16 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[q][mt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave; s0 < nsteps; s0 += NW * GS) {
+    // the j-th K-step of this wave is 2 (wave + 8 (j / 2)) + j % 2: the two halves of each
+    // 128-byte line of a row are read by one wave, back to back
+    for (int j0 = 0; 2 * (wave + NW * (j0 >> 1)) < nsteps; j0 += GS) {
       uint4 av[GS][MT], bv[GS][NT];
 #pragma unroll
       for (int u = 0; u < GS; ++u) {                 // every load of the group first
-        const int s = s0 + NW * u;
-        const int ko = s < nsteps ? s * 32 : 0;      // past the end: a valid address, masked below
+        const int j = j0 + u;
+        int st = 2 * (wave + NW * (j >> 1)) + (j & 1);
+        st = st < nsteps ? st + rot : 0;             // past the end: a valid address, masked below
+        const int ko = (st >= nsteps ? st - nsteps : st) * 32;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16_stream(mp[mt] + ko);
 #pragma unroll
@@ -165,7 +180,8 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
       }
 #pragma unroll
       for (int u = 0; u < GS; ++u) {
-        if (s0 + NW * u >= nsteps) continue;          // wave-uniform
+        const int j = j0 + u;
+        if (2 * (wave + NW * (j >> 1)) + (j & 1) >= nsteps) continue;      // wave-uniform
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8_t A = __builtin_bit_cast(bf16x8_t, mv[mt] ? av[u][mt] : z4);
@@ -188,10 +204,10 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
         red[wave][mt * NT + t][lane] = v;
       }
     __syncthreads();
-    if (wave < MT * NT) {                            // wave w finishes tile w
-      const int mt = wave / NT, t = wave % NT;
-      const f32x4_t v = ((red[0][wave][lane] + red[1][wave][lane]) + (red[2][wave][lane] + red[3][wave][lane])) +
-                        ((red[4][wave][lane] + red[5][wave][lane]) + (red[6][wave][lane] + red[7][wave][lane]));
+    for (int tile = wave; tile < MT * NT; tile += NW) {   // wave w finishes tiles w, w + 8
+      const int mt = tile / NT, t = tile % NT;
+      const f32x4_t v = ((red[0][tile][lane] + red[1][tile][lane]) + (red[2][tile][lane] + red[3][tile][lane])) +
+                        ((red[4][tile][lane] + red[5][tile][lane]) + (red[6][tile][lane] + red[7][tile][lane]));
       const int n = n0 + 16 * t + (lane & 15);
       const int mb = m0 + 16 * mt + 4 * (lane >> 4);
       if (n < a.B) {
@@ -209,7 +225,9 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
               if (a.keys_out) a.keys_out[(size_t)n * a.rows + m] = key;
             } else {
               const uint64_t cnd = pack_cand(key, (uint32_t)m);
-              bc = cnd > bc ? cnd : bc;
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt)
+                if (tt == t) bc[tt] = cnd > bc[tt] ? cnd : bc[tt];
               if (a.logits) a.logits[(size_t)n * a.rows + m] = v[i];
             }
           }
@@ -227,89 +245,20 @@ __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
     __syncthreads();
   }
   if (EPI == EPI_ARGMAX && wave < MT * NT) {
-    uint64_t o = __shfl_xor(bc, 16, kWave);
-    bc = o > bc ? o : bc;
-    o = __shfl_xor(bc, 32, kWave);
-    bc = o > bc ? o : bc;
-    const int n = n0 + 16 * (wave % NT) + lane;
-    if (lane < 16 && n < a.B) atomicMax((unsigned long long*)&a.best[(size_t)n * kBestStride], (unsigned long long)bc);
-  }
-}
-
-// Eight consecutive elements of h (bf16 or fp32 storage) from byte address src as floats;
-// zeros if !ok (src must still be a readable address: the load is unconditional).
-__device__ __forceinline__ void h_piece8(float (&hv)[8], const char* src, int h_bf16, bool ok) {
-  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-  if (h_bf16) {
-    const uint4 x = *reinterpret_cast<const uint4*>(src);
-    const uint32_t w[4] = {x.x & m, x.y & m, x.z & m, x.w & m};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { hv[2 * j] = bf16_lo(w[j]); hv[2 * j + 1] = bf16_hi(w[j]); }
-  } else {
-    const uint4 x = reinterpret_cast<const uint4*>(src)[0];
-    const uint4 y = reinterpret_cast<const uint4*>(src)[1];
-    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) hv[j] = __uint_as_float(w[j] & m);
-  }
-}
-
-// rows_dot with h read from memory (L2) piece by piece instead of held in registers: the same
-// fused multiply-adds in the same order per row, so the results are bitwise those of rows_dot
-// with load_h.  For kernels that dot the same rows with many hidden states.
-template <int RF, int CH, int NR>
-__device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, const void* h, int h_bf16, int d,
-                                                int lane, float (&out)[NR]) {
-  constexpr int EPC = Fmt<RF>::EPC;
-  const int esz = h_bf16 ? 2 : 4;
-  float acc[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int e0 = (lane + kWave * i) * EPC;
-    const bool ok = e0 < d;
-    const char* src = (const char*)h + (ok ? (size_t)e0 * esz : 0);
-    if (RF == RF_F32) {
-      float hv[4];
-      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
-      if (h_bf16) {
-        const uint2 x = *reinterpret_cast<const uint2*>(src);
-        hv[0] = bf16_lo(x.x & m); hv[1] = bf16_hi(x.x & m); hv[2] = bf16_lo(x.y & m); hv[3] = bf16_hi(x.y & m);
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(src);
-        hv[0] = __uint_as_float(x.x & m); hv[1] = __uint_as_float(x.y & m);
-        hv[2] = __uint_as_float(x.z & m); hv[3] = __uint_as_float(x.w & m);
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_F32>(g.w[r][i], hv, acc[r], 0.f);
-    } else if (RF == RF_BF16) {
-      float hv[8];
-      h_piece8(hv, src, h_bf16, ok);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_BF16>(g.w[r][i], hv, acc[r], 0.f);
-    } else {
-      float s[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {             // word j of the row chunk: elements 8 j .. 8 j + 7
-        float hv[8];
-        h_piece8(hv, src + (size_t)8 * j * esz, h_bf16, ok);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const uint32_t wj = j == 0 ? g.w[r][i].x : j == 1 ? g.w[r][i].y : j == 2 ? g.w[r][i].z : g.w[r][i].w;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) s[r] = fmaf(nib(wj, k), hv[k], s[r]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = fmaf(__uint_as_float(g.sc[r][i] << 16), s[r], acc[r]);
+    for (int t = 0; t < NT; ++t) {                 // the H tiles this wave finished
+      if (t != wave % NT && (MT * NT <= NW || NW % NT == 0)) continue;     // wave-uniform
+      uint64_t b = bc[t];
+      uint64_t o = __shfl_xor(b, 16, kWave);
+      b = o > b ? o : b;
+      o = __shfl_xor(b, 32, kWave);
+      b = o > b ? o : b;
+      const int n = n0 + 16 * t + lane;
+      if (lane < 16 && n < a.B && b) atomicMax((unsigned long long*)&a.best[(size_t)n * kBestStride], (unsigned long long)b);
     }
   }
-#pragma unroll
-  for (int r = 0; r < NR; ++r) out[r] = wave_sum(acc[r]);
 }
+
 
 // ------------------------------------------------------------------ probe selection
 // k_select: one 1024-thread workgroup per row of keys, held in registers as order-preserving
@@ -820,22 +769,41 @@ static bool use_mfma(const HeadShape& s, int fmt) {
   return s.B > 1 && s.h_bf16 && fmt == RF_BF16 && (s.d % 32) == 0;
 }
 
+// Compute units of the current device, looked up once per device.
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cached[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int NT, int EPI>
-static void launch_mfma_nt(const MfmaParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_mfma<NT, EPI>), grid, dim3(kMfmaThreads), 0, st, p);
+static void launch_mfma_nt(const MfmaParams& p, int mt, dim3 grid, hipStream_t st) {
+  if (mt == 2)      hipLaunchKernelGGL((k_mfma<NT, 2, EPI>), grid, dim3(kMfmaThreads), 0, st, p);
+  else if (mt == 3) hipLaunchKernelGGL((k_mfma<NT, 3, EPI>), grid, dim3(kMfmaThreads), 0, st, p);
+  else              hipLaunchKernelGGL((k_mfma<NT, 4, EPI>), grid, dim3(kMfmaThreads), 0, st, p);
 }
 
 template <int EPI>
 static hipError_t launch_mfma(const MfmaParams& p, int max_wg, hipStream_t st) {
-  const int ngroups = (p.rows + 16 * kMfmaMT - 1) / (16 * kMfmaMT);
+  const int cus = device_cus();
+  int mt = 2;
+  while (mt < kMfmaMaxMT && (p.rows + 16 * mt - 1) / (16 * mt) > cus) ++mt;
+  const int ngroups = (p.rows + 16 * mt - 1) / (16 * mt);
   const int nb = (p.B + 63) / 64;
   dim3 grid(ngroups < max_wg ? ngroups : max_wg, nb);
   const int nt = p.B >= 64 ? 4 : (p.B + 15) / 16;
   switch (nt) {
-    case 1: launch_mfma_nt<1, EPI>(p, grid, st); break;
-    case 2: launch_mfma_nt<2, EPI>(p, grid, st); break;
-    case 3: launch_mfma_nt<3, EPI>(p, grid, st); break;
-    default: launch_mfma_nt<4, EPI>(p, grid, st); break;
+    case 1: launch_mfma_nt<1, EPI>(p, mt, grid, st); break;
+    case 2: launch_mfma_nt<2, EPI>(p, mt, grid, st); break;
+    case 3: launch_mfma_nt<3, EPI>(p, mt, grid, st); break;
+    default: launch_mfma_nt<4, EPI>(p, mt, grid, st); break;
   }
   return hipGetLastError();
 }

@@ -65,4 +65,80 @@ __device__ __forceinline__ void rows_dot(const RowGroup<RF, CH, NR>& g, const HR
   }
 }
 
+
+// Eight consecutive elements of h (bf16 or fp32 storage) from byte address src as floats;
+// zeros if !ok (src must still be a readable address: the load is unconditional).
+__device__ __forceinline__ void h_piece8(float (&hv)[8], const char* src, int h_bf16, bool ok) {
+  const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+  if (h_bf16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {x.x & m, x.y & m, x.z & m, x.w & m};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { hv[2 * j] = bf16_lo(w[j]); hv[2 * j + 1] = bf16_hi(w[j]); }
+  } else {
+    const uint4 x = reinterpret_cast<const uint4*>(src)[0];
+    const uint4 y = reinterpret_cast<const uint4*>(src)[1];
+    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) hv[j] = __uint_as_float(w[j] & m);
+  }
+}
+
+// rows_dot with h read from memory (L2) piece by piece instead of held in registers: the same
+// fused multiply-adds in the same order per row, so the results are bitwise those of rows_dot
+// with load_h.  For kernels that dot the same rows with many hidden states.
+template <int RF, int CH, int NR>
+__device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, const void* h, int h_bf16, int d,
+                                                int lane, float (&out)[NR]) {
+  constexpr int EPC = Fmt<RF>::EPC;
+  const int esz = h_bf16 ? 2 : 4;
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int e0 = (lane + kWave * i) * EPC;
+    const bool ok = e0 < d;
+    const char* src = (const char*)h + (ok ? (size_t)e0 * esz : 0);
+    if (RF == RF_F32) {
+      float hv[4];
+      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      if (h_bf16) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        hv[0] = bf16_lo(x.x & m); hv[1] = bf16_hi(x.x & m); hv[2] = bf16_lo(x.y & m); hv[3] = bf16_hi(x.y & m);
+      } else {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        hv[0] = __uint_as_float(x.x & m); hv[1] = __uint_as_float(x.y & m);
+        hv[2] = __uint_as_float(x.z & m); hv[3] = __uint_as_float(x.w & m);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_F32>(g.w[r][i], hv, acc[r], 0.f);
+    } else if (RF == RF_BF16) {
+      float hv[8];
+      h_piece8(hv, src, h_bf16, ok);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_BF16>(g.w[r][i], hv, acc[r], 0.f);
+    } else {
+      float s[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {             // word j of the row chunk: elements 8 j .. 8 j + 7
+        float hv[8];
+        h_piece8(hv, src + (size_t)8 * j * esz, h_bf16, ok);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t wj = j == 0 ? g.w[r][i].x : j == 1 ? g.w[r][i].y : j == 2 ? g.w[r][i].z : g.w[r][i].w;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) s[r] = fmaf(nib(wj, k), hv[k], s[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] = fmaf(__uint_as_float(g.sc[r][i] << 16), s[r], acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) out[r] = wave_sum(acc[r]);
+}
+
 }  // namespace fh

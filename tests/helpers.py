@@ -59,7 +59,8 @@ def L_gemv(fmt: str, d: int) -> int:
 
 def L_mfma(d: int, B: int = None) -> int:
     """Rounding depth of the batched MFMA product for a batch of B rows (None: the largest over B)."""
-    steps = -(-(-(-d // 32)) // 8)
+    npairs = -(-(-(-d // 32)) // 2)           # K-steps of 32 columns, handed to the waves in pairs
+    steps = 2 * (-(-npairs // 8))              # steps of the busiest of the 8 waves
     levels = {1: 0, 2: 1, 4: 2}
 
     def depth(acc):
