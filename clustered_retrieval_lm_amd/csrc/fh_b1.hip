@@ -190,8 +190,10 @@ __device__ __forceinline__ int kept_count_below(const uint64_t* words, int k) {
 //    the items with h % 256 == g: cluster k has an item there exactly when the thread holding
 //    its key (t = k % 1024) satisfies (g - t * gpp) % 256 < gpp, so those threads list the
 //    workgroup's certain items as soon as bin b is known, and the tile loads start before the
-//    boundary keys are ranked, with no block-wide numbering of the kept clusters.  The number
-//    of items per workgroup is about p gpp / 256, the kept clusters spreading over residues.
+//    boundary keys are ranked, with no block-wide numbering of the kept clusters; wave 0 ranks
+//    the boundary keys and takes the workgroup's items of the kept ones itself, so no other
+//    wave waits for the ranking.  The number of items per workgroup is about p gpp / 256, the
+//    kept clusters spreading over residues.
 //  * with fewer workgroups (p < 256), with more items than a workgroup can list, or after the
 //    general selection, the kept clusters are numbered 0 .. p-1 by ascending id (certain ones
 //    first) and workgroup g takes the numbers g, g + G, ... (ranks from the kept bitmap).
@@ -336,12 +338,32 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     n_def = p;
     itemized = false;
   }
+  if (itemized && Q.nitems > kItemMax) {   // block-uniform
+    // more certain items than the list holds: number the kept clusters instead (the certain
+    // bitmap from the keys again, the same bins)
+    uint32_t wlo = 0u, whi = 0u;
+    const float* kb = a.keys;
+    asm volatile("" : "+s"(kb));            // fresh addresses here: none are kept from the first reads
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float v = kb[s * NT + tid];
+      const int bn = (int)fminf(fmaxf(fmaf(v, inv, off), 0.f), (float)(kSelBins - 1));
+      const uint64_t m = __ballot(bn > b && s * NT + tid < c);
+      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
+      put_lane(whi, (uint32_t)(m >> 32), s);
+    }
+    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
+    itemized = false;
+    __syncthreads();
+  }
   const int rb = row_bytes_of(RF, a.d);
   const int spr = a.d >> 7;
-  const int n1 = itemized ? min(Q.nitems, kItemMax) : 0;   // certain items listed so far
+  const int n1 = itemized ? Q.nitems : 0;  // this workgroup's items of certain clusters
   // ---- this wave's first item, when certain: requested while wave 0 ranks the boundary keys
   RowGroup<RF, CH, NR> g0;
   int tl0 = 0, k0 = -1;
+  int bnd_id = 0, bnd_j = 0;                // wave 0, item mode: kept boundary clusters ...
+  uint64_t bnd_mask = 0;                    // ... whose items this workgroup owns (lanes)
   HRaw<RF, CH> hraw;
   if constexpr (kEarlyH) load_h_raw<RF, CH>(hraw, a.h, a.h_bf16, a.d, lane);
   if (fast) {
@@ -372,37 +394,17 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
         const int iq = __builtin_amdgcn_readlane(it, q);
         rank += (xq > xt || (xq == xt && iq < it)) ? 1 : 0;
       }
-      if (act && rank < need) {
-        wm_set<NS>(Q.bw, it);
-        const int jb = (me - it * gpp) & (kB1Workgroups - 1);
-        if (itemized && jb < gpp) {
-          const int pos = atomicAdd(&Q.nitems, 1);
-          if (pos < kItemMax) Q.items[pos] = (it << 8) | jb;
-        }
-      }
+      const bool kept = act && rank < need;
+      if (kept && (want || !itemized)) wm_set<NS>(Q.bw, it);
+      // item mode: wave 0 itself takes this workgroup's items of kept boundary clusters
+      bnd_id = it;
+      bnd_j = (me - it * gpp) & (kB1Workgroups - 1);
+      bnd_mask = __ballot(kept && itemized && bnd_j < gpp);
     }
   }
-  __syncthreads();                                                          // 6
-  const int n2 = itemized ? Q.nitems : 0;   // every item of this workgroup
-  if (itemized && n2 > kItemMax) {
-    // more items than the list holds: number the kept clusters instead (the certain bitmap from
-    // the keys again, the same bins, plus the kept boundary clusters); the early load is dropped
-    uint32_t wlo = 0u, whi = 0u;
-    const float* kb = a.keys;
-    asm volatile("" : "+s"(kb));            // fresh addresses here: none are kept from the first reads
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const float v = kb[s * NT + tid];
-      const int bn = (int)fminf(fmaxf(fmaf(v, inv, off), 0.f), (float)(kSelBins - 1));
-      const uint64_t m = __ballot(bn > b && s * NT + tid < c);
-      put_lane(wlo, (uint32_t)m, s);                                 // the ballot into lane s
-      put_lane(whi, (uint32_t)(m >> 32), s);
-    }
-    if (lane < NS) Q.words[wave * NS + lane] = ((uint64_t)whi << 32) | wlo;
-    itemized = false;
-    k0 = -1;
-    __syncthreads();
-  }
+  // numbered mode and probe outputs need the kept boundary clusters in Q.bw; item mode
+  // without probe outputs goes on without waiting for the ranking
+  if (!itemized || want) __syncthreads();                                   // 6
   // ---- probe outputs: the kept clusters are Q.words | Q.bw (Q.bw is empty after the general
   //      selection); workgroup 0 writes their ids in ascending order
   if (want && me == 0 && a.probe_out) {
@@ -419,34 +421,14 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   }
   // numbered mode: numbers below n_def are the ascending certain clusters (Q.words), the rest
   // the kept clusters of the boundary bin (Q.bw)
-  const int nit = itemized ? n2 : (me < p ? (p - me + G - 1) / G : 0) * gpp;
+  const int nit = itemized ? n1 : (me < p ? (p - me + G - 1) / G : 0) * gpp;
   // ---- stage 2 on this workgroup's items
   HRegs<RF, CH> hr;
   if constexpr (kEarlyH) unpack_h<RF, CH>(hr, hraw, a.h_bf16);
   else load_h<RF, CH>(hr, a.h, a.h_bf16, a.d, lane);
   uint64_t bc = 0;
-  for (int it = wave; it < nit; it += NWAVE) {
-    int k, tl, j0;
-    RowGroup<RF, CH, NR> g;
-    if (it == wave && k0 >= 0) {
-      k = k0;
-      tl = tl0;
-      j0 = itemized ? (Q.items[it] & 255) * NR : (it - (it / gpp) * gpp) * NR;
-      g = g0;
-    } else {
-      if (itemized) {
-        k = Q.items[it] >> 8;
-        j0 = (Q.items[it] & 255) * NR;
-      } else {
-        const int qi = it / gpp, q = me + qi * G;
-        j0 = (it - qi * gpp) * NR;
-        k = q < n_def ? kept_rank_id<NS>(Q.words, q) : kept_rank_id<NS>(Q.bw, q - n_def);
-      }
-      const size_t row0 = (size_t)k * a.b;
-      tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
-      rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
-                        spr, lane);
-    }
+  // dot products, tokens and probe outputs of one item (cluster k, rows j0 .. j0 + NR - 1)
+  auto item = [&](int k, int j0, int tl, const RowGroup<RF, CH, NR>& g) {
     float z[NR];
     rows_dot<RF, CH>(g, hr, z);
     const int qo = want ? kept_count_below<NS>(Q.words, k) + kept_count_below<NS>(Q.bw, k) : 0;
@@ -466,6 +448,40 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
         }
       }
     }
+  };
+  auto load_item = [&](int k, int j0, int& tl, RowGroup<RF, CH, NR>& g) {
+    const size_t row0 = (size_t)k * a.b;
+    tl = (lane < NR && j0 + lane < a.b) ? a.c2t[row0 + j0 + lane] : 0;
+    rows_load<RF, CH>(g, a.tiles + row0 * rb, rb, j0, a.b, RF == RF_INT4 ? a.scales + row0 * spr : nullptr,
+                      spr, lane);
+  };
+  for (int it = wave; it < nit; it += NWAVE) {
+    if (it == wave && k0 >= 0) {
+      item(k0, itemized ? (Q.items[it] & 255) * NR : (it - (it / gpp) * gpp) * NR, tl0, g0);
+      continue;
+    }
+    int k, j0, tl;
+    if (itemized) {
+      k = Q.items[it] >> 8;
+      j0 = (Q.items[it] & 255) * NR;
+    } else {
+      const int qi = it / gpp, q = me + qi * G;
+      j0 = (it - qi * gpp) * NR;
+      k = q < n_def ? kept_rank_id<NS>(Q.words, q) : kept_rank_id<NS>(Q.bw, q - n_def);
+    }
+    RowGroup<RF, CH, NR> g;
+    load_item(k, j0, tl, g);
+    item(k, j0, tl, g);
+  }
+  // item mode: wave 0 takes this workgroup's items of the kept boundary clusters
+  for (uint64_t m = bnd_mask; m; m &= m - 1ull) {
+    const int L = __builtin_ctzll(m);
+    const int k = __builtin_amdgcn_readlane(bnd_id, L);
+    const int j0 = __builtin_amdgcn_readlane(bnd_j, L) * NR;
+    int tl;
+    RowGroup<RF, CH, NR> g;
+    load_item(k, j0, tl, g);
+    item(k, j0, tl, g);
   }
   if (lane == 0) Q.wmax[wave] = bc;
   __syncthreads();

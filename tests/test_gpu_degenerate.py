@@ -38,6 +38,10 @@ def _check_exact(dev: DeviceHead, h: np.ndarray, C: np.ndarray, C2T: np.ndarray,
     assert np.array_equal(got["probe_tokens"][0], ref.tokens[0])
     assert np.array_equal(got["probe_logits"][0].astype(np.float64), ref.z[0])
     assert got["token"][0] == ref.token[0]
+    # the token-only call (no probe outputs) takes other paths through the selection: the same token
+    tok = dev.forward(to_device(h, dev.device), p, probes=False)["token"]
+    torch.cuda.synchronize()
+    assert int(tok.cpu()[0]) == ref.token[0]
     return got, ref
 
 
@@ -54,9 +58,12 @@ def test_all_keys_equal(gpu, c, p, dt):
     assert got["token"][0] == C2T[:p].min()                            # every logit is 0
 
 
-@pytest.mark.parametrize("c,p,run", [(1003, 250, 100), (8016, 256, 300), (16384, 512, 700)])
-def test_equal_run_across_the_boundary(gpu, c, p, run):
-    d, b, dt = 128, 16, "bf16"
+@pytest.mark.parametrize("c,p,run,dt", [(1003, 250, 100, "bf16"), (8016, 256, 300, "bf16"), (16384, 512, 700, "bf16"),
+                                        # runs short enough for the one-histogram path: up to 64 tied keys
+                                        # at the boundary, many of them kept
+                                        (16384, 512, 30, "f32"), (8016, 256, 20, "f32"), (4008, 256, 50, "f32")])
+def test_equal_run_across_the_boundary(gpu, c, p, run, dt):
+    d, b = 128, 16
     hd = workloads.make_small(d, b * c, c, 1, seed=7 * c + p, dtype=dt)
     C2T = H.latent_clusters(hd.latent, c)
     Cf = np.zeros((c, d))
