@@ -253,7 +253,9 @@ fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void*
  * An empty slot of a padded C2T (entry -1, see flashhead_pack) gathers nothing: it is never the
  * token, and out->probe_tokens / probe_logits report it as -1 / -inf.
  * Limits of this build: d % 8 == 0, d <= 4096 (bf16 rows), <= 2048 (f32 rows), d % 128 == 0
- * and d <= 8192 (int4 rows); c <= 32768; 1 <= b <= 256; V < 2^31; B <= 65535.
+ * and d <= 8192 (int4 rows), each bound applying to both the centroids' and the tiles' format
+ * (so d > 4096 needs int4 centroids and int4 tiles); c <= 32768; 1 <= b <= 256; V < 2^31;
+ * B <= 65535.  Beyond them the call returns FH_ERR_UNSUPPORTED before any launch.
  */
 fh_status flashhead_forward(const fh_desc* desc, const void* h, const void* centroids,
                             const int32_t* cluster_tokens, const void* E_tiles,
