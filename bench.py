@@ -581,7 +581,7 @@ def main() -> int:
 
     if B == 1:
         units = {
-            "k_b1_scores (centroid scores, key histogram)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
+            "k_b1_scores (centroid scores)": (sc_bytes, t_sc, ["fh::k_b1_scores"]),
             "k_b1_stage2 + k_finalize_parts (selection, probe logits, token)":
                 (s2_bytes, t_s2, ["fh::k_b1_stage2", "fh::k_finalize_parts"]),
         }
