@@ -373,6 +373,10 @@ def dense_block(hd: Head, mode: str, t_call: float, alg: int, B: int, tau: float
             continue
         out[kind] = {"us_per_call": round(t_d * 1e6, 2), "bytes": nbytes, "achieved_GBps": round(nbytes / t_d / 1e9, 1),
                      "speedup": round(t_d / t_call, 2), "byte_ratio": round(nbytes / alg, 2)}
+        if kind == "int4":
+            out[kind]["note"] = ("int4 rows unpacked on the vector ALUs by a row GEMV"
+                                 + (", one pass over E per hidden state" if B > 1 else "")
+                                 + ": VALU-bound, a weak comparator; the bf16 dense head is the reference")
     return out
 
 
