@@ -26,9 +26,8 @@ struct Sampling {
 // atomic maxima of different rows never contend for a cache line.
 constexpr int kBestStride = 16;
 
-// B = 1: the fused selection + stage 2 runs kB1Threads threads per workgroup, each holding
-// b1_key_slots(c) / kB1Threads keys (a power of two >= 2); the workspace keys are padded to
-// b1_key_slots(c).
+// B = 1: the fused selection + stage 2 runs kB1Threads threads per workgroup; the workspace
+// keys are padded to b1_key_slots(c) (a multiple of kB1Threads, at least 2 of them).
 constexpr int kB1Threads = 1024;
 constexpr int kB1Workgroups = 256;
 __host__ __device__ inline int b1_key_slots(int c) {
@@ -37,10 +36,34 @@ __host__ __device__ inline int b1_key_slots(int c) {
   return s * kB1Threads;
 }
 
+// B = 1 candidate lists, written by stage 1 and read by the fused selection.  Stage 1 runs one
+// workgroup of g / 4 waves per group of g consecutive clusters and lists the m = min(g, 16)
+// largest keys of its group in descending order (key desc, id asc) as packed entries
+// (ord key << 32 | ~id): group w's entries are lst[w m .. w m + m).  Slots past c in the last
+// group hold entries whose high word is 0 (they decode to NaN and rank below every key).  The
+// top p of the c keys equals the top p of the L = ngroups m entries unless some group with
+// m < g has its m-th entry among those p (then it may hold more); R entries are real keys.
+// g = 64 needs 1024-thread workgroups, whose rows fit in registers up to 3 chunk slots; groups
+// are chosen large enough to cut the entries, small enough to keep >= 240 workgroups busy.
+struct B1Lists {
+  int g, m, ngroups, L, R;
+};
+inline B1Lists b1_lists(int c, int chunk_slots_c) {
+  B1Lists l;
+  l.g = (chunk_slots_c <= 3 && (c + 63) / 64 >= 240) ? 64 : (c + 31) / 32 >= 240 ? 32 : 16;
+  l.m = l.g < 16 ? l.g : 16;
+  l.ngroups = (c + l.g - 1) / l.g;
+  l.L = l.ngroups * l.m;
+  const int last = c - (l.ngroups - 1) * l.g;
+  l.R = (l.ngroups - 1) * l.m + (last < l.m ? last : l.m);
+  return l;
+}
+
 // Workspace carve-up (all offsets 256-byte aligned): keys, masks, best, probes; the
 // regions stage 1 writes come first so their offsets do not depend on p.
 struct Workspace {
   float* keys;        // [B][c] stage-1 keys
+  uint64_t* lst;      // B = 1: the candidate lists (B1Lists), up to c + 64 entries
   int32_t* probes;    // [B][p] kept clusters, ascending
   uint64_t* best;     // [B][kBestStride] packed (key, ~token) maxima (element 0 of each line)
   uint64_t* part;     // [256] per-workgroup maxima of the fused B = 1 stage 2
@@ -78,6 +101,8 @@ struct B1Args {
   uint64_t seed, step;
   float* keys;
   float* keys_out;
+  uint64_t* lst;
+  int c_slots;                // chunk slots of the centroid rows (fixes the list shape)
   uint64_t* part;
   const int32_t* c2t;
   const void* tiles;

@@ -709,6 +709,11 @@ Workspace carve_workspace(void* base, int B, int c, int p) {
   char* b = (char*)base;
   w.keys = (float*)(b ? b + off : nullptr);
   off = up(off + (B == 1 ? (size_t)b1_key_slots(c) : (size_t)B * c) * sizeof(float));
+  w.lst = nullptr;
+  if (B == 1) {
+    w.lst = (uint64_t*)(b ? b + off : nullptr);
+    off = up(off + ((size_t)c + 64) * sizeof(uint64_t));
+  }
 
   w.mask = nullptr;
   w.kflag = nullptr;
@@ -817,7 +822,7 @@ hipError_t launch_scores(const HeadShape& s, const void* h, const void* C, const
     B1Args a{};
     a.h = h; a.C = C; a.c_scales = c_scales; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b;
     a.sample = smp.sample; a.tau = smp.tau; a.seed = smp.seed; a.step = smp.step;
-    a.keys = ws.keys; a.keys_out = keys_out;
+    a.keys = ws.keys; a.keys_out = keys_out; a.lst = ws.lst; a.c_slots = chunk_slots(s.c_fmt, s.d);
     return s.c_fmt == RF_F32 ? launch_b1_scores_f32(a, st)
          : s.c_fmt == RF_BF16 ? launch_b1_scores_bf16(a, st) : launch_b1_scores_int4(a, st);
   }
@@ -896,7 +901,7 @@ hipError_t launch_stage2_b1(const HeadShape& s, int p, const void* h, const int3
   B1Args a{};
   a.h = h; a.h_bf16 = s.h_bf16; a.c = s.c; a.d = s.d; a.b = s.b; a.p = p;
   a.sample = smp.sample; a.tau = smp.tau; a.seed = smp.seed; a.step = smp.step;
-  a.keys = ws.keys; a.part = ws.part;
+  a.keys = ws.keys; a.part = ws.part; a.lst = ws.lst; a.c_slots = chunk_slots(s.c_fmt, s.d);
   a.c2t = c2t; a.tiles = tiles; a.scales = scales;
   a.probe_out = probe_out; a.logits_out = logits_out; a.tokens_out = tokens_out; a.token = token;
   return s.e_fmt == RF_F32 ? launch_b1_stage2_f32(a, st)

@@ -50,7 +50,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("FLASHHEAD_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise FileNotFoundError(f"{p} not built: run __graft_entry__.build() or "
                                 "python -m clustered_retrieval_lm_amd.build")

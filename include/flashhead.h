@@ -229,7 +229,10 @@ fh_status flashhead_probe_logits(const fh_desc* desc, int64_t p, const void* h,
  * non-NULL).  Reads the keys the last flashhead_centroid_scores call left in `workspace`, so
  * flashhead_centroid_scores + flashhead_select_and_probe is flashhead_forward.  At B = 1 the
  * selection and the probed logits run in one kernel: every workgroup selects the same kept
- * set and scores its share of it.  Arguments as for flashhead_probe_logits.
+ * set and scores its share of it, from per-group candidate lists that stage 1 also leaves in
+ * the workspace (each group of consecutive clusters lists its largest keys; the selection over
+ * the lists is exact and falls back to all c keys when a list may have been cut short).
+ * Arguments as for flashhead_probe_logits.
  */
 fh_status flashhead_select_and_probe(const fh_desc* desc, int64_t p, const void* h,
                                      const int32_t* cluster_tokens, const void* E_tiles,

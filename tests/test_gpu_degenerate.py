@@ -122,3 +122,25 @@ def test_few_keys_far_above(gpu, c, p, n_high, dt):
     dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
     got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
     assert set(high.tolist()) <= set(got["probe_ids"][0].tolist())
+
+
+@pytest.mark.parametrize("n_top,dt", [(64, "f32"), (64, "bf16"), (16, "bf16"), (15, "f32")])
+def test_one_group_holds_many_kept_keys(gpu, n_top, dt):
+    # Stage 1 lists the 16 largest keys of every group of 64 consecutive clusters (d = 64, so
+    # c = 16384 takes 64-cluster groups).  Here n_top clusters of group 1 (ids 64 ..) hold the
+    # largest keys: with n_top >= 16 the group's list is cut short inside the top p and the
+    # selection must fall back to all c keys; with 15 the lists hold the whole top p.  Scores
+    # are small integers (exact in bf16 and fp32): the result must be the oracle's bit for bit.
+    c, p, d, b = 16384, 100, 64, 16
+    hd = workloads.make_small(d, b * c, c, 1, seed=500 + n_top, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    Cf = np.zeros((c, d))
+    Cf[:, 0] = (np.arange(c) * 37) % 97
+    Cf[64:64 + n_top, 0] = 200.0 + 2.0 * np.arange(n_top)
+    C = _storage(Cf, dt)
+    hf = np.zeros((1, d))
+    hf[0, 0] = 1.0
+    h = _storage(hf, dt)
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
+    assert set(range(64, 64 + n_top)) <= set(got["probe_ids"][0].tolist())
