@@ -122,9 +122,15 @@ struct MfmaParams {
 template <int NT, int MT, int EPI>
 __global__ __launch_bounds__(kMfmaThreads) void k_mfma(MfmaParams a) {
   constexpr int NW = kMfmaWaves;
-  // K-steps per load group (register budget: the group's loads, MT + NT 16-byte words a step)
-  constexpr int GS = MT + NT <= 3 ? 8 : MT + NT <= 6 ? 4 : 2;
   constexpr int NACC = NT == 1 ? 4 : NT == 2 ? 2 : 1;
+  // K-steps per load group.  A CU keeps only about 64 KB of loads in flight, so a workgroup's
+  // C and H bytes take several memory round trips whatever the grouping; with one H tile
+  // (B <= 16) the group holds every step of the wave (up to 36 16-byte words of loads per lane,
+  // a multiple of NACC so that step j always feeds accumulator j % NACC) and its loads queue
+  // behind each other without an MFMA phase between them (int4 B = 16: 16.7 us instead of 19.4);
+  // with more H tiles, groups of 2 - 4 steps measured faster (Qwen B = 64: 14.0 against 15.3)
+  constexpr int GS0 = 36 / (MT + NT);
+  constexpr int GS = NT == 1 ? (GS0 - GS0 % NACC > NACC ? GS0 - GS0 % NACC : NACC) : MT + NT <= 6 ? 4 : 2;
   __shared__ f32x4_t red[NW][MT * NT][kWave];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = blockIdx.y * 64;
