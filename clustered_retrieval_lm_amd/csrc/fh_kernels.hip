@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_tiles_probe(TileParams a) {
 // group is read from HBM once and reused from registers for those rows.
 // SAMPLE: the token keys carry Gumbel noise (the greedy instantiation leaves out the Philox
 // code and its registers).
-template <int RF, int CH, bool SAMPLE>
+template <int RF, int CH, bool SAMPLE, bool HB = false>
 __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rb = row_bytes_of(RF, a.d);
@@ -408,18 +408,21 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
           const int r = wi * 64 + __builtin_ctzll(bits);
           bits &= bits - 1ull;
           if (r >= a.B) continue;                   // only if the workspace holds no masks
-          // the row words are opaque per hidden row: their conversions are redone for each row
-          // instead of being hoisted out of this loop (which would hold every converted element
-          // of the four rows in registers)
+          // fp32 and int4 row words are opaque per hidden row: their conversions are redone for
+          // each row instead of being hoisted out of this loop (which would hold every converted
+          // element of the four rows in registers; measured slower).  bf16 rows with bf16 h are
+          // dotted as raw words, with nothing to hoist, and left to the scheduler
+          if (!(RF == RF_BF16 && HB)) {
 #pragma unroll
-          for (int i = 0; i < kRPI; ++i)
+            for (int i = 0; i < kRPI; ++i)
 #pragma unroll
-            for (int q = 0; q < CH; ++q) {
-              asm volatile("" : "+v"(g.w[i][q].x), "+v"(g.w[i][q].y), "+v"(g.w[i][q].z), "+v"(g.w[i][q].w));
-              asm volatile("" : "+v"(g.sc[i][q]));
-            }
+              for (int q = 0; q < CH; ++q) {
+                asm volatile("" : "+v"(g.w[i][q].x), "+v"(g.w[i][q].y), "+v"(g.w[i][q].z), "+v"(g.w[i][q].w));
+                asm volatile("" : "+v"(g.sc[i][q]));
+              }
+          }
           float z[kRPI];
-          rows_dot_stream<RF, CH>(g, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane, z);
+          rows_dot_stream<RF, CH, kRPI, HB>(g, (const char*)a.h + (size_t)r * a.d * hsz, a.h_bf16, a.d, lane, z);
           // position of k in row r's ascending probe list (probe outputs only)
           int lo = 0;
           if (want) {
@@ -888,6 +891,8 @@ hipError_t launch_tiles(const HeadShape& s, int p, const void* h, const int32_t*
     else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_F32, kCH, false>), grid, dim3(kThreads), 0, st, a)); }
   } else if (s.e_fmt == RF_BF16) {
     if (b1) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_probe<RF_BF16, kCH>), grid, dim3(kThreads), 0, st, a)); }
+    else if (s.h_bf16 && smp.sample) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, true, true>), grid, dim3(kThreads), 0, st, a)); }
+    else if (s.h_bf16) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, false, true>), grid, dim3(kThreads), 0, st, a)); }
     else if (smp.sample) { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, true>), grid, dim3(kThreads), 0, st, a)); }
     else    { FH_DISPATCH_CH(ch, hipLaunchKernelGGL((k_tiles_mask<RF_BF16, kCH, false>), grid, dim3(kThreads), 0, st, a)); }
   } else {

@@ -8,6 +8,7 @@
 namespace fh {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRPI = 4;          // rows per wave per row-dot step
@@ -84,10 +85,17 @@ __device__ __forceinline__ void h_piece8(float (&hv)[8], const char* src, int h_
   }
 }
 
-// rows_dot with h read from memory (L2) piece by piece instead of held in registers: the same
-// fused multiply-adds in the same order per row, so the results are bitwise those of rows_dot
-// with load_h.  For kernels that dot the same rows with many hidden states.
-template <int RF, int CH, int NR>
+// rows_dot with h read from memory (L2) piece by piece instead of held in registers, for kernels
+// that dot the same rows with many hidden states.  fp32 and int4 rows, and bf16 rows with fp32 h:
+// the same fused multiply-adds in the same order per row as rows_dot with load_h (bitwise the
+// same results).  bf16 rows with bf16 h: the raw words go straight into v_dot2c_f32_bf16 (two
+// exact bf16 products and the running sum per instruction, four per 16-byte chunk), with no
+// bf16 -> fp32 unpacking of either operand; measured on random operands over 2^+-14 magnitudes,
+// with cancelling products and with zero, tiny and huge running sums, one instruction's error
+// stays below 2.8 u (|p0| + |p1| + |acc|), u = 2^-24, so a lane's chain of 4 CH instructions
+// counts as at most 16 CH roundings.  HB: h is bf16 (compile time, so the chunk loop has no
+// branch).
+template <int RF, int CH, int NR, bool HB = false>
 __device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, const void* h, int h_bf16, int d,
                                                 int lane, float (&out)[NR]) {
   constexpr int EPC = Fmt<RF>::EPC;
@@ -114,10 +122,24 @@ __device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, c
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_F32>(g.w[r][i], hv, acc[r], 0.f);
     } else if (RF == RF_BF16) {
-      float hv[8];
-      h_piece8(hv, src, h_bf16, ok);
+      if (HB) {                                  // h is bf16 (HB): packed bf16 dots on the raw words
+        const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        const uint32_t hw[4] = {x.x & m, x.y & m, x.z & m, x.w & m};
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_BF16>(g.w[r][i], hv, acc[r], 0.f);
+        for (int r = 0; r < NR; ++r) {
+          const uint32_t ww[4] = {g.w[r][i].x, g.w[r][i].y, g.w[r][i].z, g.w[r][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ww[q]),
+                                                     __builtin_bit_cast(bf16x2_t, hw[q]), acc[r], false);
+        }
+      } else {
+        float hv[8];
+        h_piece8(hv, src, h_bf16, ok);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = chunk_dot<RF_BF16>(g.w[r][i], hv, acc[r], 0.f);
+      }
     } else {
       float s[NR];
 #pragma unroll

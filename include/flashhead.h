@@ -320,7 +320,8 @@ fh_status flashhead_dense_workspace_bytes(const fh_desc* desc, size_t* bytes);
 /*
  * The dense head the paper starts from (Section 3): z = E h over all V tokens, then argmax
  * (greedy) or argmax z / tau + G(U(seed, r, step, 1, t)) (sampling), ties to the smaller id.
- * The same token keys as flashhead_forward's stage 2, so p = c gives identical tokens.
+ * The same token keys as flashhead_forward's stage 2 (the same noise on logits that agree up
+ * to fp32 rounding), so p = c gives the same token unless the top two keys are that close.
  *   E       device [V][d] token-major, desc->e_dtype F32 | BF16 | INT4_G128; INT4_G128 is one
  *           buffer: the nibbles [V][d/2] (the tile format of flashhead_pack), then from byte
  *           round_up(V d / 2, 256) the bf16 group scales [V][d/128] -- the layout

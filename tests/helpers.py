@@ -16,6 +16,9 @@ multiply-adds, tree levels): |fl(s) - s| <= gamma_L * sum_j |h_j x_j|, gamma_L =
 u = 2^-24 (Higham, "Accuracy and Stability of Numerical Algorithms", Sec. 3.1).  Each kernel
 path's L follows from its accumulation order:
   row GEMV (16-byte chunks, 64 lanes): L = CH * EPC + 6   (per-lane FMA chain, 6 butterfly levels)
+  B > 1 stage 2, bf16 rows and bf16 h:  L = 16 * CH + 6    (per-lane chain of 4 CH v_dot2c_f32_bf16, each
+                                        counted as 4 roundings: its error, measured on the GPU, stays
+                                        below 2.8 u (|p0| + |p1| + |acc|))
   int4 rows:                            L = 32 + CH + 7    (32-product chunk sum, scaled chain, tree)
   bf16 MFMA 16x16x32, K split 8 ways:   L = 6 * ceil(S / A) + log2(A) + 3, S = ceil(d / 256) K-steps per
                                         wave, A = 4 / 2 / 1 accumulators per tile when the batch spans
@@ -55,6 +58,14 @@ def L_gemv(fmt: str, d: int) -> int:
     if fmt == "int4":
         return 32 + ch + 7
     return ch * EPC[fmt] + 6
+
+
+def L_stage2(B: int, h_dtype: str, e_dtype: str, d: int) -> int:
+    """Rounding depth of the stage-2 logits: the batched kernel dots bf16 rows with bf16 h by
+    packed bf16 dot instructions, every other path by the row GEMV's FMA chain."""
+    if B > 1 and h_dtype == "bf16" and e_dtype == "bf16":
+        return 16 * chunk_slots("bf16", d) + 6
+    return L_gemv(e_dtype, d)
 
 
 def L_mfma(d: int, B: int = None) -> int:

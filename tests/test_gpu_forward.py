@@ -52,7 +52,7 @@ def _run_and_compare(dev: DeviceHead, hd_h: np.ndarray, h_dtype: str, C, C2T, ti
     rows = range(B) if rows is None else rows
     ref = ohead.forward(hd_h, h_dtype, C, dev.c_dtype, C2T, tiles, p, mode=mode, tau=tau, seed=seed, step=step)
     L1 = H.L_stage1(B, h_dtype, dev.c_dtype, dev.d)
-    L2 = H.L_gemv(dev.e_dtype, dev.d)
+    L2 = H.L_stage2(B, h_dtype, dev.e_dtype, dev.d)
     for r in rows:
         H.compare_row(ref, r, got["probe_ids"][r], got["probe_logits"][r], got["probe_tokens"][r],
                       got["token"][r], p, L1, L2, mode == "sample", tau, seed, step, fp32, rep, got_keys=keys_np[r])

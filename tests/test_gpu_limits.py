@@ -1,7 +1,8 @@
 """GPU parity at the edges of the supported shapes, and at the Llama-3.2-1B c/p sweep shapes.
 
-Limits (include/flashhead.h): c up to 32768 clusters (the B = 1 selection then holds 32 keys
-per thread, the batched one 8 per thread in four-key blocks), bf16 rows up to d = 4096, fp32
+Limits (include/flashhead.h): c up to 32768 clusters (the B = 1 selection then ranks 8192
+candidate-list entries, 8 per thread; the batched one holds 8 keys per thread in four-key
+blocks), bf16 rows up to d = 4096, fp32
 rows up to d = 2048, int4 rows up to d = 8192 (the centroids' format bounds d too, so
 d = 8192 needs int4 centroids).  The sweep of the FlashHead paper's Table 7
 varies the cluster size at the Llama-3.2-1B head shape (d = 2048, V = 128256): b = 32
@@ -25,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 LIMITS = [
     # d, b, c, B, p, dtype, e_dtype
-    (64, 2, 32768, 1, 600, "bf16", "bf16"),      # the largest c: 32 key slots per thread at B = 1
+    (64, 2, 32768, 1, 600, "bf16", "bf16"),      # the largest c: 8192 list entries at B = 1
     (64, 2, 32768, 3, 300, "bf16", "bf16"),      # ... and 8 four-key blocks per thread at B > 1
     (4096, 16, 300, 1, 20, "bf16", "bf16"),      # the longest bf16 rows: 8 chunk slots per lane
     (4096, 16, 300, 5, 20, "bf16", "bf16"),      # ... through the MFMA stage 1

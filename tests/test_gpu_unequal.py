@@ -56,7 +56,7 @@ def test_padded_clusters_match_the_oracle(gpu, d, V, c, B, p, et, mode):
     h = to_device(hd.h, gpu)
     rep = H.Report()
     L1 = H.L_stage1(B, dt, dt, d)
-    L2 = H.L_gemv(et, d)
+    L2 = H.L_stage2(B, dt, et, d)
     for step in ([0] if mode == "greedy" else [0, 1, 2]):
         out = dev.forward(h, p, mode=mode, tau=0.8, seed=3, step=step)
         torch.cuda.synchronize()
