@@ -377,6 +377,22 @@ def dense_block(hd: Head, mode: str, t_call: float, alg: int, B: int, tau: float
             out[kind]["note"] = ("int4 rows unpacked on the vector ALUs by a row GEMV"
                                  + (", one pass over E per hidden state" if B > 1 else "")
                                  + ": VALU-bound, a weak comparator; the bf16 dense head is the reference")
+    # torch's linear (a library GEMM) + argmax over the same E: a second dense comparator, the
+    # faster of the two is the one the speedup is quoted against (greedy work only, so a lower
+    # bound on a dense sampling head)
+    import torch
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    E = hd.dev.E
+    if E is not None:
+        Et = E.view(tdt).view(wl.V, wl.d)
+        Ht = [x.view(tdt).view(B, wl.d) for x in hd.hidden(B)]
+        t_t = graph_seconds_per_call(torch, lambda i: torch.argmax(torch.nn.functional.linear(Ht[i % len(Ht)], Et),
+                                                                   dim=-1), 20, 5)
+        nb = wl.V * row_bytes(wl.dtype, wl.d)
+        out["torch_linear_argmax"] = {"us_per_call": round(t_t * 1e6, 2), "bytes": nb,
+                                      "achieved_GBps": round(nb / t_t / 1e9, 1), "speedup": round(t_t / t_call, 2)}
+        fastest = min(v["us_per_call"] for k, v in out.items() if v and k in (wl.dtype, "torch_linear_argmax"))
+        out["speedup_vs_fastest_dense"] = round(fastest * 1e-6 / t_call, 2)
     return out
 
 
@@ -609,12 +625,6 @@ def main() -> int:
         dd = dense.get(wl.dtype)
         if dd:
             read_ceiling, ceiling_src = dd["achieved_GBps"], f"flashhead_dense_forward streaming {dd['bytes'] / 1e6:.0f} MB"
-        tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-        Et = dv.E.view(tdt).view(wl.V, wl.d)
-        Ht = [x.view(tdt).view(B, wl.d) for x in hd.hidden(B)]
-        t_t = graph_seconds_per_call(torch, lambda i: torch.argmax(torch.nn.functional.linear(Ht[i % len(Ht)], Et),
-                                                                   dim=-1), 20, 5)
-        dense["torch_linear_argmax_us"] = round(t_t * 1e6, 2)
         log(f"dense head {dense}")
     big = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)
     t_big = graph_seconds_per_call(torch, lambda i: big.sum(), 5, 3)
