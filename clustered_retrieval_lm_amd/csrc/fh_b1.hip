@@ -40,6 +40,7 @@ struct B1Params {
   float* keys_out;      // optional copy of the keys (staged entry point)
   uint64_t* lst;        // candidate lists (B1Lists)
   int L, R;             // list entries (R of them real keys)
+  int ng;               // groups: the lists are rank-major, entry (group, rank r) at r ng + group
   int use_list;         // the lists suit this p (else the selection runs over all keys)
   int fullable;         // m < g: a group's list may be cut short (its last entry is lst[16 w + 15])
   uint64_t* part;       // [gridDim.x] per-workgroup maxima of k_b1_stage2
@@ -55,7 +56,9 @@ struct B1Params {
 // ------------------------------------------------------------------ stage 1
 
 // One workgroup of NWG waves per group of G = 4 NWG consecutive clusters: the keys, then the
-// group's M = min(G, 16) largest in descending order (key desc, id asc) into lst[group M ..).
+// group's M = min(G, 16) largest in descending order (key desc, id asc): the entry of rank r goes to
+// lst[r ngroups + group] (rank-major: a wave of the selection then holds one rank per list slot, and
+// the waves holding ranks far down the lists skip the work of certain entries as a whole).
 // The rank of an entry is the number of the group's entries that are larger as packed
 // (ord key, ~id) values; every wave counts those among its own four and the counts meet in LDS.
 template <int RF, int CH, int NWG>
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(NWG * 64) void k_b1_scores(B1Params a) {
   __syncthreads();
   if (tid < G) {
     const int r = rk[tid];
-    if (r < M) a.lst[(size_t)blockIdx.x * M + r] = pk[tid];
+    if (r < M) a.lst[(size_t)r * gridDim.x + blockIdx.x] = pk[tid];
   }
 }
 
@@ -112,7 +115,6 @@ constexpr int kItemMax = 256;              // (cluster, row group) items one wor
 
 struct S2Shared {
   float wmx[16], wmn[16];
-  int wtot[16];
   int bnd[3];                              // boundary bin, entries above it, entries in it
   int ncand, nitems, full;
   float cx[kS2MaxCand];                    // the boundary bin's keys ...
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
                   p * gpp <= (kItemMax / 4) * kB1Workgroups;
   bool fast = a.use_list != 0;                                                              // block-uniform
   // ---- list entries; past L, and the pads of a short last group, decode to NaN: ignored by
-  //      min / max, never greater or equal, and never counted
+  //      min / max, never greater or equal, and counted in bin 0 only
   uint64_t e[NL];
   float x[NL];
 #pragma unroll
@@ -193,52 +195,50 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   float hi = Q.wmx[0], lo = Q.wmn[0];
 #pragma unroll
   for (int w = 1; w < NWAVE; ++w) { hi = fmaxf(hi, Q.wmx[w]); lo = fminf(lo, Q.wmn[w]); }
-  const float inv = (float)kSelBins / (hi - lo);
+  // the bins only need a map that is monotone in the key and the same in every thread, so the
+  // hardware reciprocal serves
+  const float inv = (float)kSelBins * __builtin_amdgcn_rcpf(hi - lo);
   fast = fast && hi > lo && inv > 0.f && inv < 3.0e38f;
   const float off = -lo * inv;
+  // a NaN entry (a pad) falls in bin 0 (fmaxf returns the number): harmless, as the fast path
+  // needs the boundary above bin 0, so bin 0 is never kept, ranked or counted above the boundary
   int bins[NL];
   if (fast) {
 #pragma unroll
     for (int s = 0; s < NL; ++s) {
-      bins[s] = x[s] == x[s] ? (int)fminf(fmaxf(fmaf(x[s], inv, off), 0.f), (float)(kSelBins - 1)) : -1;
-      if (bins[s] >= 0) atomicAdd(&S.hist[bins[s]], 1);
+      bins[s] = (int)fminf(fmaxf(fmaf(x[s], inv, off), 0.f), (float)(kSelBins - 1));
+      atomicAdd(&S.hist[bins[s]], 1);
     }
   }
   __syncthreads();                                                          // 2
-  // ---- boundary bin: wave w scans bins [2048 - 128 (w + 1), 2048 - 128 w) from the top
-  const int top = kSelBins - 1 - 128 * wave - 2 * lane;
-  int h_lo = 0, h_hi = 0, incl = 0;
-  if (fast) {
-    const int2 hh = *reinterpret_cast<const int2*>(&S.hist[top - 1]);
-    h_lo = hh.x;
-    h_hi = hh.y;
-    incl = wave_incl_scan(h_lo + h_hi);
-    if (lane == 63) Q.wtot[wave] = incl;
+  // ---- boundary bin, found by wave 0 alone (one instruction costs a quarter of the issue slots it
+  //      would take in every wave): lane l sums the 32 bins [2048 - 32 (l + 1), 2048 - 32 l), a
+  //      scan from the top finds the slice holding the p-th entry, and a second scan over that
+  //      slice's bins finds the bin.  No bin reaching p leaves bnd zero: the general selection.
+  if (fast && wave == 0) {
+    const int4* hp = reinterpret_cast<const int4*>(&S.hist[kSelBins - 32 * (lane + 1)]);
+    int v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int4 q = hp[i];
+      v += (q.x + q.y) + (q.z + q.w);
+    }
+    const int incl = wave_incl_scan(v);
+    const int L = __ffsll((unsigned long long)__ballot(incl >= p)) - 1;
+    if (L >= 0) {                           // wave-uniform
+      const int before = L > 0 ? __builtin_amdgcn_readlane(incl, L - 1) : 0;
+      const int bin = kSelBins - 32 * L - 1 - lane;
+      const int hv = lane < 32 ? S.hist[bin > 0 ? bin : 0] : 0;
+      const int incl2 = wave_incl_scan(hv) + before;
+      const int J = __ffsll((unsigned long long)__ballot(lane < 32 && incl2 >= p)) - 1;
+      if (lane == J) {
+        Q.bnd[0] = bin;
+        Q.bnd[1] = incl2 - hv;
+        Q.bnd[2] = hv;
+      }
+    }
   }
   __syncthreads();                                                          // 3
-  if (fast) {
-    int before = 0, bw = -1;
-#pragma unroll
-    for (int w = 0; w < NWAVE; ++w) {
-      const int t = Q.wtot[w];
-      if (bw < 0) {
-        if (before + t >= p) bw = w;
-        else before += t;
-      }
-    }
-    if (wave == bw) {                       // the slice holding the p-th entry resolves it
-      const int cum = incl + before;
-      const int L = __ffsll((unsigned long long)__ballot(cum >= p)) - 1;
-      const int ex = cum - h_lo - h_hi;
-      if (lane == L) {
-        const bool upper = ex + h_hi >= p;
-        Q.bnd[0] = upper ? top : top - 1;
-        Q.bnd[1] = upper ? ex : ex + h_hi;
-        Q.bnd[2] = upper ? h_hi : h_lo;
-      }
-    }
-  }
-  __syncthreads();                                                          // 4
   int b = 0, above = 0, inb = 0;
   if (fast) {
     b = Q.bnd[0];
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
     for (int s = 0; s < NL; ++s) {
       const int id = (int)(0xFFFFFFFFu - (uint32_t)e[s]);
       const bool cert = bins[s] > b;
-      if (a.fullable && bins[s] >= b && ((s * NT + tid) & 15) == 15) Q.full = 1;
+      if (a.fullable && bins[s] >= b && s * NT + tid >= a.L - a.ng) Q.full = 1;   // a group's last entry
       if (cert) {
         const int jme = (me - id * gpp) & (kB1Workgroups - 1);     // this workgroup's row group of id
         if (itemized && jme < gpp) {
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
       }
     }
   }
-  __syncthreads();                                                          // 5
+  __syncthreads();                                                          // 4
   if (fast) fast = Q.ncand == inb && !Q.full;          // block-uniform
   if (!fast) {                              // the general selection over all c keys
     for (int i = tid; i < kSelBins; i += NT) S.hist[i] = 0;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   // numbering and probe outputs need the whole kept bitmap and its prefix offsets (the general
   // selection built both); item mode without probe outputs goes on without waiting for the ranking
   if (fast && (!itemized || want)) {        // block-uniform
-    __syncthreads();                                                        // 6
+    __syncthreads();                                                        // 5
     bitmap_prefix(c, S);
   }
   // ---- probe outputs: workgroup 0 writes the kept ids in ascending order
@@ -476,7 +476,7 @@ static B1Params params_of(const B1Args& x) {
   a.sample = x.sample; a.tau = x.tau; a.rng = make_rng(x.seed, x.step);
   a.keys = x.keys; a.keys_out = x.keys_out; a.part = x.part;
   const B1Lists l = b1_lists(x.c, x.c_slots);
-  a.lst = x.lst; a.L = l.L; a.R = l.R;
+  a.lst = x.lst; a.L = l.L; a.R = l.R; a.ng = l.ngroups;
   a.fullable = l.m < l.g;
   a.use_list = (l.m == l.g || (long)l.g * x.p <= 4L * x.c) && l.R >= x.p && l.L <= 8192;
   a.c2t = x.c2t; a.tiles = (const char*)x.tiles; a.scales = x.scales;
