@@ -336,10 +336,38 @@ __device__ __forceinline__ float chunk_dot<RF_BF16>(const uint4 w, const float* 
   return acc;
 }
 
-// int4: 32 two's-complement nibbles, element 2i in the low nibble of byte i.  The 32
-// products q h are summed first (each is exact in fp32), then scaled by the group's s.
-__device__ __forceinline__ float nib(uint32_t w, int k) {
-  return (float)((int32_t)(w << (28 - 4 * k)) >> 28);
+// int4: 32 two's-complement nibbles, element 2i in the low nibble of byte i, so element 8j + k
+// of a chunk is nibble k of its word j.  The 32 products q h are summed first (each is exact in
+// fp32), then scaled by the group's s.
+//
+// The nibbles are decoded in pairs (k, k + 4) straight into fp16, with no integer-to-float
+// conversion.  In the word (shifted right by 8 bits for k = 2, 3) nibble k sits in bits 0..3
+// (k = 0, 2) or 4..7 (k = 1, 3) of the low half and nibble k + 4 at the same place in the high
+// half; keeping those bits, flipping each nibble's top bit (q + 8 instead of two's complement)
+// and setting the exponent field of 1024 makes each half 1024 + (q + 8), or 1024 + 16 (q + 8)
+// for odd k, which is exact; one packed fp16 add (or multiply-add by 1/16) leaves q exactly.  Each half feeds one mixed-precision fused multiply-add (v_fma_mix_f32),
+// which widens it exactly, so the chain of fused multiply-adds is the one of a float decode:
+// 17 instructions per 8 elements instead of 24.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void nib_pairs(uint32_t w, half2_t (&q)[4]) {
+  const uint32_t y = w >> 8;                          // nibbles 2, 3, 6, 7 where 0, 1, 4, 5 were
+  const half2_t a = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u);   // 0 and 4
+  const half2_t b = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ 0x64806480u);   // 1 and 5
+  const half2_t c = __builtin_bit_cast(half2_t, (y & 0x000F000Fu) ^ 0x64086408u);   // 2 and 6
+  const half2_t e = __builtin_bit_cast(half2_t, (y & 0x00F000F0u) ^ 0x64806480u);   // 3 and 7
+  const half2_t off = {(_Float16)-1032.f, (_Float16)-1032.f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.f, (_Float16)-72.f};
+  q[0] = a + off;
+  q[1] = b * sixteenth + off16;
+  q[2] = c + off;
+  q[3] = e * sixteenth + off16;
+}
+
+// Element k (0..7) of a word decoded by nib_pairs.
+__device__ __forceinline__ float nib_of(const half2_t (&q)[4], int k) {
+  return (float)(k < 4 ? q[k].x : q[k - 4].y);
 }
 
 template <>
@@ -348,8 +376,10 @@ __device__ __forceinline__ float chunk_dot<RF_INT4>(const uint4 w, const float* 
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    half2_t q[4];
+    nib_pairs(ws[j], q);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s = fmaf(nib(ws[j], k), hv[8 * j + k], s);
+    for (int k = 0; k < 8; ++k) s = fmaf(nib_of(q, k), hv[8 * j + k], s);
   }
   return fmaf(scale, s, acc);
 }

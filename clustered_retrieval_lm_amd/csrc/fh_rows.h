@@ -151,8 +151,10 @@ __device__ __forceinline__ void rows_dot_stream(const RowGroup<RF, CH, NR>& g, c
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const uint32_t wj = j == 0 ? g.w[r][i].x : j == 1 ? g.w[r][i].y : j == 2 ? g.w[r][i].z : g.w[r][i].w;
+          half2_t q[4];
+          nib_pairs(wj, q);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) s[r] = fmaf(nib(wj, k), hv[k], s[r]);
+          for (int k = 0; k < 8; ++k) s[r] = fmaf(nib_of(q, k), hv[k], s[r]);
         }
       }
 #pragma unroll
