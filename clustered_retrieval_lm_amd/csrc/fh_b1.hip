@@ -429,22 +429,19 @@ __global__ __launch_bounds__(kB1Threads) void k_b1_stage2(B1Params a) {
   }
 }
 
-// The token: the largest of the per-workgroup maxima part[0 .. n).  (Templated on the row
-// format only so that each object of this file has its own copy.)
+// The token: the largest of the per-workgroup maxima part[0 .. n), n <= 256, by one wave (each lane
+// reduces four of them, then a butterfly of lane shuffles: no barrier).  (Templated on the row format
+// only so that each object of this file has its own copy.)
 template <int RF>
-__global__ __launch_bounds__(256) void k_finalize_parts(const uint64_t* part, int n, int32_t* token) {
-  __shared__ uint64_t wm[4];
-  const int tid = threadIdx.x;
-  uint64_t m = 0;
-  for (int i = tid; i < n; i += 256) m = part[i] > m ? part[i] : m;
-  m = wave_max_u64(m);
-  if ((tid & 63) == 0) wm[tid >> 6] = m;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t r = wm[0];
-    for (int w = 1; w < 4; ++w) r = wm[w] > r ? wm[w] : r;
-    token[0] = (int32_t)cand_id(r);
-  }
+__global__ __launch_bounds__(64) void k_finalize_parts(const uint64_t* part, int n, int32_t* token) {
+  const int lane = threadIdx.x;
+  uint64_t v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = lane + 64 * q < n ? part[lane + 64 * q] : 0ull;     // all loads first
+  uint64_t m = v[0] > v[1] ? v[0] : v[1];
+  const uint64_t m2 = v[2] > v[3] ? v[2] : v[3];
+  m = wave_max_u64(m > m2 ? m : m2);
+  if (lane == 0) token[0] = (int32_t)cand_id(m);
 }
 
 // ------------------------------------------------------------------ launchers (row format FH_B1_RF)
@@ -523,7 +520,7 @@ static void launch_stage2_ch(const B1Params& a, hipStream_t st) {
   if (!a.use_list || a.L <= 2 * kB1Threads) launch_stage2_nl<CH, 2>(a, G, nr, st);
   else if (a.L <= 4 * kB1Threads)           launch_stage2_nl<CH, 4>(a, G, nr, st);
   else                                      launch_stage2_nl<CH, 8>(a, G, nr, st);
-  hipLaunchKernelGGL(k_finalize_parts<kRF>, dim3(1), dim3(256), 0, st, (const uint64_t*)a.part, G, a.token);
+  hipLaunchKernelGGL(k_finalize_parts<kRF>, dim3(1), dim3(64), 0, st, (const uint64_t*)a.part, G, a.token);
 }
 
 #if FH_B1_RF == 0
