@@ -100,6 +100,35 @@ def measured_traffic(workload: str, kernels) -> "int | None":
     return total
 
 
+def profiled_us(tag: str, kernels) -> "dict | None":
+    """Average rocprofv3 durations (us) of `kernels` (name prefixes) from profiles/kernel_trace_<tag>.txt.
+
+    That file is the --kernel-trace --stats summary of this script on the same workload; where
+    a kernel has several instantiations the one launched most often (the head's) is taken.  None
+    when the file is missing, lacks a kernel, or was taken on other library sources.
+    """
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.txt")
+    if not os.path.exists(path):
+        return None
+    sha, rows = None, []
+    for line in open(path):
+        if line.startswith("# library sources sha256"):
+            sha = line.rsplit(":", 1)[1].strip()
+        elif line.strip() and not line.startswith("#") and not line.startswith("kernel "):
+            f = line[78:].split()
+            if len(f) == 6:
+                name = re.sub(r"^void\s+", "", line[:78].strip())
+                rows.append((re.sub(r"[<(].*$", "", name), int(f[0]), float(f[2])))
+    if sha != source_sha256():
+        return None
+    out = {}
+    for k in kernels:
+        hits = [r for r in rows if r[0] == k]
+        if hits:
+            out[k] = max(hits, key=lambda r: r[1])[2]
+    return out or None
+
+
 def capture(torch, launch, n_calls, first=0):
     """A graph of launch(first) .. launch(first + n_calls - 1) (captured, not executed)."""
     g = torch.cuda.CUDAGraph()
@@ -616,6 +645,16 @@ def main() -> int:
     dom_gbs = dom_bytes / dom_t / 1e9
     tag = f"{args.workload}_b{B}" if args.mode == "greedy" else None
     traffic = measured_traffic(tag, dom_kernels) if tag else None
+    # the same unit from the committed rocprofv3 trace (the profiler adds a few us to tiny kernels)
+    ptag = args.workload if args.workload.endswith(f"_b{B}") else f"{args.workload}_b{B}"
+    prof = profiled_us(ptag, dom_kernels) if args.mode == "greedy" else None
+    profiled = None
+    if prof:
+        main_k = max(prof, key=prof.get)
+        profiled = {"source": f"profiles/kernel_trace_{ptag}.txt", "avg_us": prof,
+                    "unit_frac": round(dom_bytes / (sum(prof.values()) * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                    "main_kernel": main_k,
+                    "main_kernel_frac": round(dom_bytes / (prof[main_k] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
 
     # ---- comparators and the streaming-read ceiling
     dense = None
@@ -738,7 +777,8 @@ def main() -> int:
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_t * 1e6, 3),
-                     "whole_call_frac": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4)},
+                     "whole_call_frac": round(alg_bytes / t_call / 1e9 / PEAK_HBM_GBS, 4),
+                     "profiled": profiled},
         "kernels": {k: {"bytes_per_launch": b_, "us_per_launch": round(t_ * 1e6, 3),
                         "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_, _) in units.items()},
         "dense": dense,
