@@ -144,3 +144,33 @@ def test_one_group_holds_many_kept_keys(gpu, n_top, dt):
     dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
     got, _ = _check_exact(dev, h, C, C2T, ohead.pack_tiles(hd.E, dt, C2T, dt), dt, p)
     assert set(range(64, 64 + n_top)) <= set(got["probe_ids"][0].tolist())
+
+
+@pytest.mark.parametrize("c,p", [(1003, 37), (9496, 256), (16384, 512)])
+def test_batched_tied_and_one_hot_rows(gpu, c, p):
+    """B > 1 (the batched MFMA stage 1, the per-row selection and the per-cluster stage 2): rows
+    whose keys all tie (h = 0) and a one-hot row whose keys are single exact products (bf16
+    centroids repeat values, so it has ties as well).  Every score and logit is exact on both
+    sides, so the probe lists (ascending ids, ties to the smaller id), probe logits and tokens
+    must match the oracle bit for bit in every row."""
+    d, b, dt = 64, 16, "bf16"
+    hd = workloads.make_small(d, b * c, c, 1, seed=c + p + 1, dtype=dt)
+    C2T = H.latent_clusters(hd.latent, c)
+    C = _storage(np.random.default_rng(c + 1).standard_normal((c, d)), dt)
+    h = np.zeros((3, d), dtype=np.uint16)
+    h[1, 5] = 0x3F80                               # bf16 1.0
+    dev = DeviceHead(d, b * c, c, C, C2T, hd.E, dt, dt, dt, dt, device=gpu)
+    tiles = ohead.pack_tiles(hd.E, dt, C2T, dt)
+    out = dev.forward(to_device(h, gpu), p)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    ref = ohead.forward(h, dt, C, dt, C2T, tiles, p)
+    for r in range(3):
+        assert np.array_equal(got["probe_ids"][r], ref.probe_ids[r]), f"row {r}"
+        assert np.array_equal(got["probe_tokens"][r], ref.tokens[r]), f"row {r}"
+        assert np.array_equal(got["probe_logits"][r].astype(np.float64), ref.z[r]), f"row {r}"
+        assert got["token"][r] == ref.token[r], f"row {r}"
+    assert np.array_equal(got["probe_ids"][0], np.arange(p)) and np.array_equal(got["probe_ids"][2], np.arange(p))
+    tok = dev.forward(to_device(h, gpu), p, probes=False)["token"]
+    torch.cuda.synchronize()
+    assert np.array_equal(tok.cpu().numpy(), ref.token)
