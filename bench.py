@@ -426,12 +426,19 @@ def dense_block(hd: Head, mode: str, t_call: float, alg: int, B: int, tau: float
 
 
 def run_sweep(args) -> int:
+    """`--sweep`: the grid and the unequal-cluster ablation alone, one JSON line."""
+    print(json.dumps(sweep_block()), flush=True)
+    return 0
+
+
+def sweep_block() -> dict:
     """The clusters / probes grid of the paper's Table 7 at the Llama-3.2-1B head shape
     (d = 2048, V = 128256, bf16): c in {4008, 8016, 16032} (b = 32, 16, 8), p in {128, 256, 512},
     greedy, B = 1, timed like the configurations (graph replay over R centroid / tile copies and
     R hidden states), with the dense head as the comparator.  Synthetic heads of the workloads
     recipe whose latent partition serves as the balanced clustering (latency does not depend on
-    which balanced clustering is used).  Prints one JSON line."""
+    which balanced clustering is used).  Then the same head's tokens in unequal clusters (Table 6):
+    a padded C2T, timed against the equal clusters.  Returns the JSON object of both."""
     import numpy as np
     import torch
 
@@ -530,14 +537,12 @@ def run_sweep(args) -> int:
         log(f"unequal clusters (b_max={bmax}) p={p}: {t * 1e6:.2f} us/call vs equal {eq['us_per_call']} us")
     del dev, Cs, Ts, Hs, hd
     torch.cuda.empty_cache()
-    print(json.dumps({"sweep": "clusters x probes (FlashHead Table 7 grid), Llama-3.2-1B head shape, bf16, "
-                               "B=1, greedy, synthetic", "dense": dense, "rows": rows,
-                      "unequal_clusters": {"what": "Table 6 ablation: 8016 clusters of lognormal sizes (sigma 0.5, "
-                                                   "mean 16) as a C2T padded to the largest cluster",
-                                           "b_max": int(bmax), "size_min": int(sizes.min()),
-                                           "size_mean": round(float(sizes.mean()), 2), "rows": unequal}}),
-          flush=True)
-    return 0
+    return {"sweep": "clusters x probes (FlashHead Table 7 grid), Llama-3.2-1B head shape, bf16, "
+                     "B=1, greedy, synthetic", "dense": dense, "rows": rows,
+            "unequal_clusters": {"what": "Table 6 ablation: 8016 clusters of lognormal sizes (sigma 0.5, "
+                                         "mean 16) as a C2T padded to the largest cluster",
+                                 "b_max": int(bmax), "size_min": int(sizes.min()),
+                                 "size_mean": round(float(sizes.mean()), 2), "rows": unequal}}
 
 
 # configurations carried in the line besides the headline: (workload, mode)
@@ -557,7 +562,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-head comparator")
     ap.add_argument("--no-mc", action="store_true", help="skip the Monte-Carlo marginal (N = 10^4 probe sets)")
-    ap.add_argument("--no-configs", action="store_true", help="only the headline workload")
+    ap.add_argument("--no-configs", action="store_true", help="only the headline workload (no configurations, no sweep)")
+    ap.add_argument("--no-sweep", action="store_true", help="leave out the clusters x probes grid")
     ap.add_argument("--mc-sets", type=int, default=10000, help="probe sets of the Monte-Carlo marginal")
     ap.add_argument("--sweep", action="store_true",
                     help="only the clusters x probes grid (Table 7) at the Llama-3.2-1B head shape")
@@ -747,6 +753,16 @@ def main() -> int:
                 configs.append(r)
             if h2 is not hd:
                 del h2
+    # ---- the clusters x probes grid and the unequal-cluster ablation (Tables 7 and 6)
+    sweep = None
+    if not args.no_configs and not args.no_sweep:
+        if hd is not None:
+            del hd
+            hd = None
+        torch.cuda.empty_cache()
+        t_sw = time.time()
+        sweep = sweep_block()
+        log(f"sweep done in {time.time() - t_sw:.1f} s")
     res = {
         "metric": "head calls/s + achieved HBM GB/s vs dense LM head, B=1 Gemma-3-1B shape",
         "value": round(1.0 / t_call, 1),
@@ -783,6 +799,7 @@ def main() -> int:
                         "GBps": round(b_ / t_ / 1e9, 1)} for k, (b_, t_, _) in units.items()},
         "dense": dense,
         "configs": configs,
+        "sweep": sweep,
         "mc_marginal": mc,
         "cpu_baseline": cpu,
     }
