@@ -385,6 +385,11 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
   const int hsz = a.h_bf16 ? 2 : 4;
   const bool want = a.logits_out || a.tokens_out;
   __shared__ uint64_t wbest[2][4];
+  // SAMPLE: the 4 waves' logits and tokens of the tile rows for one hidden row meet in LDS, and
+  // wave 0 draws the 16 Gumbel keys on 16 lanes (one Philox evaluation per token, instead of each
+  // wave running it with 4 of its lanes active)
+  __shared__ float zbuf[2][4 * kRPI];
+  __shared__ int tbuf[2][4 * kRPI];
   int par = 0;
   // workgroup g takes entries g, g + G, ... of the list of clusters kept by any row
   const int nk = *a.nkept;
@@ -438,15 +443,36 @@ __global__ __launch_bounds__(kThreads) void k_tiles_mask(TileParams a) {
             const float zi = lane_pick<kRPI>(z, lane);
             const int t = lane_pick<kRPI>(tj, lane);
             const int j = j0 + lane;
+            if (SAMPLE && lane < kRPI) {             // past the tile: no token
+              zbuf[par][wave * kRPI + lane] = zi;
+              tbuf[par][wave * kRPI + lane] = j < a.b ? t : -1;
+            }
             if (lane < kRPI && j < a.b) {
-              if (t >= 0) {                          // an empty slot (-1) is never chosen
-                const float key = make_key(zi, SAMPLE, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+              if (!SAMPLE && t >= 0) {               // an empty slot (-1) is never chosen
+                const float key = make_key(zi, false, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
                 bc = pack_cand(key, (uint32_t)t);
               }
               const size_t o = ((size_t)r * a.p + lo) * a.b + j;
               if (a.logits_out) a.logits_out[o] = t >= 0 ? zi : -__builtin_huge_valf();
               if (a.tokens_out) a.tokens_out[o] = t;
             }
+          }
+          if constexpr (SAMPLE) {
+            __syncthreads();
+            if (wave == 0) {
+              uint64_t c = 0;
+              if (lane < 4 * kRPI) {
+                const int t = tbuf[par][lane];
+                if (t >= 0) {                        // an empty slot (-1) is never chosen
+                  const float key = make_key(zbuf[par][lane], true, a.tau, a.rng, (uint32_t)r, 1u, (uint32_t)t);
+                  c = pack_cand(key, (uint32_t)t);
+                }
+              }
+              c = wave_max_u64(c);
+              if (lane == 0) atomicMax((unsigned long long*)&a.best[(size_t)r * kBestStride], (unsigned long long)c);
+            }
+            par ^= 1;
+            continue;
           }
           // the four waves' maxima for row r meet in LDS: one atomic per (cluster, row)
           bc = wave_max_u64(bc);
