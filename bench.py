@@ -761,8 +761,12 @@ def main() -> int:
             hd = None
         torch.cuda.empty_cache()
         t_sw = time.time()
-        sweep = sweep_block()
-        log(f"sweep done in {time.time() - t_sw:.1f} s")
+        try:
+            sweep = sweep_block()
+            log(f"sweep done in {time.time() - t_sw:.1f} s")
+        except Exception as e:                 # the headline line is still printed
+            sweep = {"error": f"{type(e).__name__}: {e}"}
+            log(f"sweep failed: {sweep['error']}")
     res = {
         "metric": "head calls/s + achieved HBM GB/s vs dense LM head, B=1 Gemma-3-1B shape",
         "value": round(1.0 / t_call, 1),
